@@ -1,0 +1,253 @@
+/*
+ * biverify.h — C ABI of the batch-invariant verifier step for MI355X (gfx950).
+ *
+ * The verifier step of decode-verify-rollback inference: a decoder forward
+ * over W = N*K candidate tokens (K from each of N requests) built from
+ * batch-invariant RMSNorm, matmul and attention, ending in Gumbel-max
+ * verification of the candidates and an overwrite of the fast path's KV.
+ *
+ * Sources (web pages; cited by title and paragraph):
+ *   [LLM42]  Telegram post on batch-invariant kernels and LLM-42
+ *            (tgstat.com/ru/channel/@ashnskt/392):
+ *            para 1 - batch-invariant matmul (no split-K, one data-parallel
+ *            tiling), RMSNorm (fixed split over hidden), attention (fixed
+ *            KV-split size); para 3 - fast path vs fixed-batch verifier,
+ *            reference point = last known-correct token, overwrite of the
+ *            fast path's KV at every verification; para 4 - W = N*K.
+ *   [GUMBEL] Reading-club post on "Coupling without Communication and
+ *            Drafter-Invariant Speculative Decoding"
+ *            (tginsight.xyz/en/channel/AIexTime/post/185): Gumbel-max trick
+ *            (argmax of logits + Gumbel noise, noise prepared in advance);
+ *            Gumbel coupling (same noise for draft and target; verification
+ *            compares the two tokens; no draft logits needed).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named as device pointers are device memory owned by the
+ *     caller; the library never frees them.  Entry points allocate nothing
+ *     (workspaces are passed in).
+ *   - All work is enqueued asynchronously on `stream` (a hipStream_t; NULL =
+ *     the default stream).  Nothing synchronises.
+ *   - Arguments are checked on the host before anything is launched; a bad
+ *     argument returns BIV_EINVAL (or BIV_EUNSUPPORTED for a shape this build
+ *     has no kernel for) and launches nothing.  biv_last_error() then holds
+ *     a message (thread-local).  A failed launch returns BIV_EHIP.  Device
+ *     faults surface at the caller's next synchronisation.
+ *   - No C++ exception crosses this interface.
+ *   - Layouts are row-major; "[a, b]" lists dimensions slowest first.
+ *   - bf16 = IEEE binary32 truncated to its top 16 bits; every bf16 result
+ *     is rounded once from fp32, to nearest even.
+ *   - Batch invariance: for every entry point marked "_bi", each output row
+ *     is a function of that row's inputs only (its own activations, its own
+ *     request's KV); the bits do not change with M, with the number of
+ *     requests, with which other rows share the call, or with a row's
+ *     position in the batch.
+ */
+#ifndef BIVERIFY_H
+#define BIVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BIV_OK = 0,
+  BIV_EINVAL = 1,       /* bad argument: null pointer, size, alignment, dtype */
+  BIV_EUNSUPPORTED = 2, /* valid request this build has no kernel for */
+  BIV_EHIP = 3          /* the HIP runtime reported an error */
+} biv_status;
+
+typedef enum { BIV_F32 = 0, BIV_BF16 = 1 } biv_dtype;
+
+typedef void* biv_stream; /* hipStream_t */
+
+/* Version of this interface (increments when a signature changes). */
+int biv_abi_version(void);
+
+/* Message for the last non-OK status returned on the calling thread. */
+const char* biv_last_error(void);
+
+/* --------------------------------------------------------------------------
+ * rmsnorm_bi — batch-invariant RMSNorm ([LLM42] para 1: RMSNorm with a fixed
+ * split over the hidden dimension, independent of how many compute units are
+ * busy).
+ *
+ *   y[m, i] = x[m, i] * gamma[i] / sqrt(mean_k x[m, k]^2 + eps)
+ *
+ * x [M, H] in x_dt; gamma [H] and y [M, H] in y_dt (device).  The sum of
+ * squares of a row is accumulated in fp32 in an order fixed by H alone: lane
+ * t of a 256-lane workgroup adds elements t, t+256, ... in ascending order,
+ * then a fixed butterfly over lanes and a fixed ascending sum over waves.
+ * M >= 0 (M = 0 launches nothing), 1 <= H <= 65536.  x and y may not overlap.
+ * ------------------------------------------------------------------------ */
+biv_status rmsnorm_bi(const void* x, biv_dtype x_dt, const void* gamma, void* y, biv_dtype y_dt,
+                      int64_t M, int64_t H, float eps, biv_stream stream);
+
+/* --------------------------------------------------------------------------
+ * gemm_bi — batch-invariant matmul ([LLM42] para 1: no split-K; one and the
+ * same data-parallel tiling for every batch size).
+ *
+ *   acc[m, n] = sum_k A[m, k] * B[n, k]          (fp32 accumulation)
+ *   epilogue BIV_EPI_STORE:  C[m, n] = acc
+ *   epilogue BIV_EPI_ACCUM:  C[m, n] = C[m, n] + acc   (residual add, in place)
+ *
+ * A [M, K] and B [N, K] (the weight in linear-layer layout: row n holds the
+ * K inputs of output n) in in_dt; C [M, N] in out_dt (device).
+ *   in_dt BIV_BF16: bf16 MFMA (32x32x16), fp32 accumulators; every output is
+ *     reduced over k in ascending 16-wide steps by one instruction shape,
+ *     whatever M is, so a row's bits never depend on M.  Requires K % 8 == 0
+ *     and 16-byte aligned A, B.
+ *   in_dt BIV_F32: fp32 FMA chain over k ascending.
+ * The rounding of C is once, from fp32.  M >= 0, N >= 1, K >= 1.
+ * ------------------------------------------------------------------------ */
+enum { BIV_EPI_STORE = 0, BIV_EPI_ACCUM = 1 };
+
+biv_status gemm_bi(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                   biv_dtype in_dt, biv_dtype out_dt, int epilogue, biv_stream stream);
+
+/* --------------------------------------------------------------------------
+ * attn_decode_bi — batch-invariant paged decode/verify attention ([LLM42]
+ * para 1: a fixed KV-split size, no adaptation to sequence length or load;
+ * para 3-4: the verifier runs K query rows per request).
+ *
+ * Row (r, j), j < q_len, is the query of the token at absolute position
+ * ctx[r] + j; it attends to keys at positions 0 .. ctx[r] + j of request r:
+ *   out = softmax(q . k_p * scale) . v_p,  q head h reads KV head h / (Hq/Hkv).
+ *
+ * q   R*q_len rows of Hq*D elements (row r*q_len + j), consecutive rows
+ *     q_stride elements apart (>= Hq*D; a slice of a fused QKV output
+ *     can be passed directly)                      dt, device
+ * k_cache, v_cache [num_blocks, Hkv, 16, D]        dt, device (pages of 16)
+ * block_table [R, max_blocks] int32: physical page of each logical page;
+ *             entries outside [0, num_blocks) are treated as empty pages
+ *             (their keys are masked, their values read as zero).
+ * ctx [R] int32: verified context length L_r >= 0 of each request.
+ * out [R*q_len, Hq, D]                             dt, device
+ *
+ * Keys are cut into 256-token chunks aligned at absolute position 0.  Each
+ * chunk gives a partial (max, sum, weighted values) for each row; partials
+ * are left-folded in ascending chunk order within fixed segments of
+ * BIV_ATTN_SEG_TOKENS tokens, and the segment results are left-folded in
+ * ascending order.  Every split point is a fixed absolute position, so a
+ * row's result depends only on its own request's data and length.
+ * Positions >= ctx[r] + q_len read as empty (values zero, keys masked).
+ *
+ * Supported: dt BIV_BF16 with D == 128 and q_len * (Hq/Hkv) <= 32 (bf16 MFMA
+ * path); dt BIV_F32 with D in {64, 128} (fp32 path, any q_len).  Hq % Hkv == 0,
+ * ctx[r] + q_len <= max_blocks * 16.
+ *
+ * workspace: device memory of at least
+ * biv_attn_workspace_bytes(R, Hkv, max_blocks, BIV_ATTN_SEG_TOKENS) bytes (bf16
+ * path; may be NULL for the fp32 path).  It must be zero-filled before its first
+ * use; every call leaves it ready for the next one.  Calls that share a
+ * workspace must be ordered (same stream).
+ * ------------------------------------------------------------------------ */
+#define BIV_ATTN_CHUNK_TOKENS 256
+#define BIV_ATTN_SEG_TOKENS 1024
+
+size_t biv_attn_workspace_bytes(int R, int Hkv, int max_blocks, int seg_tokens);
+
+biv_status attn_decode_bi(const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, const int32_t* ctx, void* out, int R, int q_len,
+                          int Hq, int Hkv, int D, int max_blocks, int num_blocks, float scale,
+                          biv_dtype dt, void* workspace, size_t workspace_bytes, biv_stream stream);
+
+/* --------------------------------------------------------------------------
+ * gumbel_verify — Gumbel-max coupled verification ([GUMBEL]: add Gumbel(0,1)
+ * noise to the logits and take the argmax; the same noise couples draft and
+ * target, so verification compares the draft token with the target token).
+ *
+ * logits, noise [R*K, V] fp32 (row r*K + j; device).  noise row (r, j) must be
+ *   the noise of the token at position ctx[r] + j + 1 (prepared in advance).
+ * cand [R, K] int32: the fast path's candidate for position ctx[r] + j + 1.
+ * Outputs (device, always fully written):
+ *   target [R, K] int32:  argmax_v fl32(logits + noise); exact ties go to the
+ *                         lowest index; NaN never wins; -0 equals +0.
+ *   accept_len [R] int32: first j with target != cand, K if none.
+ *   next_token [R] int32: target[r, accept_len[r]], or -1 if accept_len == K.
+ * Two launches (per-row argmax, per-request decision), no workspace.
+ * ------------------------------------------------------------------------ */
+biv_status gumbel_verify(const float* logits, const float* noise, const int32_t* cand, int R, int K,
+                         int V, int32_t* target, int32_t* accept_len, int32_t* next_token,
+                         biv_stream stream);
+
+/* --------------------------------------------------------------------------
+ * kv_overwrite — write the verifier's K/V into the slots the fast path wrote
+ * ([LLM42] para 3: at every verification the fast path's KV, computed at some
+ * other batch size, is overwritten with the verifier's consistent values).
+ *
+ * k_new, v_new: T token rows of Hkv*D elements, consecutive rows src_stride
+ *   elements apart (so a slice of a fused QKV output can be passed directly).
+ * slot [T] int64: physical slot page*16 + offset of token t.
+ * k_cache, v_cache [num_blocks, Hkv, 16, D] (device), element size by dt.
+ * Bit copy; every other slot is left unchanged.  Slots outside
+ * [0, num_blocks*16) are skipped.  Slots must be distinct.
+ * ------------------------------------------------------------------------ */
+biv_status kv_overwrite(const void* k_new, const void* v_new, int64_t src_stride, const int64_t* slot,
+                        void* k_cache, void* v_cache, int T, int Hkv, int D, int num_blocks,
+                        biv_dtype dt, biv_stream stream);
+
+/* --------------------------------------------------------------------------
+ * Elementwise helpers of the decoder forward (no reductions; row-local).
+ * ------------------------------------------------------------------------ */
+
+/* out[t, :] = table[ids[t], :] converted to out_dt (bf16 -> fp32 is exact).
+ * ids outside [0, V) give a zero row.  table [V, H] in table_dt. */
+biv_status embed_rows(const int32_t* ids, const void* table, biv_dtype table_dt, void* out,
+                      biv_dtype out_dt, int T, int V, int H, biv_stream stream);
+
+/* Host-side RoPE table (rotate-half convention): for p < max_pos, i < D/2,
+ * cos_sin[(p * D/2 + i) * 2 + 0] = cos(p * theta^(-2i/D)),
+ * cos_sin[(p * D/2 + i) * 2 + 1] = sin(...), computed in fp64, rounded to fp32.
+ * cos_sin is HOST memory of max_pos * D floats. */
+biv_status biv_rope_table(float* cos_sin, int max_pos, int D, double theta);
+
+/* In-place rotate-half RoPE on n_heads heads of D elements starting at
+ * element 0 of each of T rows (row stride `stride` elements):
+ * (a, b) = (x[i], x[i + D/2]) -> (a cos - b sin, b cos + a sin), fp32 math,
+ * rounded once to dt.  pos [T] int32 absolute positions (< max_pos of the
+ * table; others leave the row unchanged).  cos_sin: device copy of the
+ * biv_rope_table output. */
+biv_status rope_apply(void* x, int64_t stride, const int32_t* pos, const float* cos_sin, int T,
+                      int n_heads, int D, int max_pos, biv_dtype dt, biv_stream stream);
+
+/* out[m, n] = silu(gu[m, n]) * gu[m, N + n], silu(g) = g / (1 + exp(-g)),
+ * fp32 math; gu [M, 2N], out [M, N], both in dt. */
+biv_status swiglu(const void* gu, void* out, int64_t M, int64_t N, biv_dtype dt, biv_stream stream);
+
+/* --------------------------------------------------------------------------
+ * Non-invariant comparison variants (same contracts as above, NOT batch
+ * invariant): what a serving engine does by default at small batch ([LLM42]
+ * para 1: split-K matmul; attention whose split adapts to length and load).
+ * ------------------------------------------------------------------------ */
+
+/* gemm_splitk: bf16 A/B as in gemm_bi, fp32 partial sums of `splits` slices
+ * of K reduced in a second pass.  splits == 0 picks the count from M, N, K so
+ * that the grid fills the GPU.  workspace: biv_splitk_workspace_bytes(). */
+size_t biv_splitk_workspace_bytes(int64_t M, int64_t N, int splits);
+/* The split count gemm_splitk uses for splits == 0. */
+int biv_splitk_auto_splits(int64_t M, int64_t N, int64_t K);
+biv_status gemm_splitk(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                       biv_dtype out_dt, int epilogue, int splits, void* workspace,
+                       size_t workspace_bytes, biv_stream stream);
+
+/* attn_decode_adaptive: bf16 attention whose segment size (tokens per
+ * workgroup, a multiple of 256) is chosen from the batch:
+ * biv_attn_adaptive_split() returns the largest split that still gives at
+ * least 512 workgroups (2 per compute unit), or the whole capacity when the
+ * batch alone gives that many.  split_tokens == 0 uses that choice.
+ * Workspace: biv_attn_workspace_bytes(R, Hkv, max_blocks, split). */
+int biv_attn_adaptive_split(int R, int Hkv, int max_blocks);
+biv_status attn_decode_adaptive(const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
+                                const int32_t* block_table, const int32_t* ctx, void* out, int R,
+                                int q_len, int Hq, int Hkv, int D, int max_blocks, int num_blocks,
+                                float scale, int split_tokens, void* workspace,
+                                size_t workspace_bytes, biv_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BIVERIFY_H */

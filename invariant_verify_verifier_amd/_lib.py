@@ -1,0 +1,283 @@
+"""ctypes binding of libbiverify (the C ABI in include/biverify.h).
+
+Argument marshalling only: every function here takes torch tensors that
+already live on the GPU, passes their addresses, sizes and torch's current
+HIP stream to the library, and raises on a non-OK status.  No computation
+happens in Python and there is no fallback: if the library is missing the
+import fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbiverify.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build the HIP library first "
+        "(python -m invariant_verify_verifier_amd.build, or __graft_entry__.build())")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+BIV_OK, BIV_EINVAL, BIV_EUNSUPPORTED, BIV_EHIP = 0, 1, 2, 3
+BIV_F32, BIV_BF16 = 0, 1
+BIV_EPI_STORE, BIV_EPI_ACCUM = 0, 1
+ATTN_CHUNK_TOKENS = 256
+ATTN_SEG_TOKENS = 1024
+
+_vp, _i32, _i64, _f32, _f64, _sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                                    ctypes.c_double, ctypes.c_size_t)
+
+_SIGS = {
+    "biv_abi_version": ([], _i32),
+    "biv_last_error": ([], ctypes.c_char_p),
+    "rmsnorm_bi": ([_vp, _i32, _vp, _vp, _i32, _i64, _i64, _f32, _vp], _i32),
+    "gemm_bi": ([_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp], _i32),
+    "biv_attn_workspace_bytes": ([_i32, _i32, _i32, _i32], _sz),
+    "attn_decode_bi": ([_vp, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                        _vp, _sz, _vp], _i32),
+    "gumbel_verify": ([_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp], _i32),
+    "kv_overwrite": ([_vp, _vp, _i64, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp], _i32),
+    "embed_rows": ([_vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp], _i32),
+    "biv_rope_table": ([_vp, _i32, _i32, _f64], _i32),
+    "rope_apply": ([_vp, _i64, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp], _i32),
+    "swiglu": ([_vp, _vp, _i64, _i64, _i32, _vp], _i32),
+    "biv_splitk_workspace_bytes": ([_i64, _i64, _i32], _sz),
+    "biv_splitk_auto_splits": ([_i64, _i64, _i64], _i32),
+    "gemm_splitk": ([_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp, _sz, _vp], _i32),
+    "biv_attn_adaptive_split": ([_i32, _i32, _i32], _i32),
+    "attn_decode_adaptive": ([_vp, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                              _vp, _sz, _vp], _i32),
+}
+
+for _name, (_args, _ret) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _ret
+
+
+class BivError(RuntimeError):
+    def __init__(self, fn, status):
+        msg = _lib.biv_last_error().decode(errors="replace")
+        super().__init__(f"{fn}: status {status}: {msg}")
+        self.status = status
+
+
+def _check(fn, status):
+    if status != BIV_OK:
+        raise BivError(fn, status)
+
+
+def exported_symbols():
+    """Names of the C entry points this binding declares."""
+    return list(_SIGS)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BIV_BF16
+    if t.dtype == torch.float32:
+        return BIV_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _p(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _same_dtype(*ts):
+    d = {t.dtype for t in ts if t is not None}
+    if len(d) != 1:
+        raise TypeError(f"dtype mismatch: {d}")
+
+
+def _want(t, dtype, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+# ----------------------------------------------------------------- entry points
+
+
+def rmsnorm_bi(x, gamma, y, eps):
+    _contig(x, gamma, y)
+    _same_dtype(gamma, y)
+    M, H = x.shape
+    assert tuple(y.shape) == (M, H) and gamma.numel() == H
+    _check("rmsnorm_bi", _lib.rmsnorm_bi(_p(x), _dt(x), _p(gamma), _p(y), _dt(y), M, H, eps, _stream()))
+    return y
+
+
+def gemm_bi(a, b, c, accumulate=False):
+    """c[M,N] (=|+=) a[M,K] @ b[N,K]^T."""
+    _contig(a, b, c)
+    M, K = a.shape
+    N = b.shape[0]
+    assert b.shape[1] == K and tuple(c.shape) == (M, N)
+    _same_dtype(a, b)
+    epi = BIV_EPI_ACCUM if accumulate else BIV_EPI_STORE
+    _check("gemm_bi", _lib.gemm_bi(_p(a), _p(b), _p(c), M, N, K, _dt(a), _dt(c), epi, _stream()))
+    return c
+
+
+def attn_workspace_bytes(R, Hkv, max_blocks, seg_tokens=ATTN_SEG_TOKENS):
+    return _lib.biv_attn_workspace_bytes(R, Hkv, max_blocks, seg_tokens)
+
+
+def _attn_checks(q, k_cache, v_cache, block_table, ctx, out, q_len):
+    """q: [T, Hq*D] row view (row stride may exceed Hq*D) or [T, Hq, D]; out [T, Hq, D] contiguous."""
+    if q.stride(-1) != 1:
+        raise ValueError("q rows must be contiguous")
+    _same_dtype(q, k_cache, v_cache, out)
+    _want(block_table, torch.int32, "block_table")
+    _want(ctx, torch.int32, "ctx")
+    T, Hq, D = out.shape
+    if q.dim() == 3:
+        assert q.stride(1) == D and tuple(q.shape) == (T, Hq, D)
+    else:
+        assert tuple(q.shape) == (T, Hq * D)
+    R, _ = block_table.shape
+    assert T == R * q_len and ctx.numel() == R
+    assert k_cache.shape == v_cache.shape and k_cache.dim() == 4 and k_cache.shape[2] == 16 and k_cache.shape[3] == D
+    return q.stride(0), Hq, D
+
+
+def attn_decode_bi(q, k_cache, v_cache, block_table, ctx, out, q_len, scale, workspace=None):
+    """q [R*q_len, Hq*D] (rows may be strided) or [R*q_len, Hq, D]; out [R*q_len, Hq, D];
+    caches [num_blocks, Hkv, 16, D]; block_table [R, max_blocks] int32; ctx [R] int32."""
+    _contig(k_cache, v_cache, block_table, ctx, out)
+    q_stride, Hq, D = _attn_checks(q, k_cache, v_cache, block_table, ctx, out, q_len)
+    R, max_blocks = block_table.shape
+    num_blocks, Hkv = k_cache.shape[0], k_cache.shape[1]
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("attn_decode_bi", _lib.attn_decode_bi(
+        _p(q), q_stride, _p(k_cache), _p(v_cache), _p(block_table), _p(ctx), _p(out), R, q_len, Hq, Hkv, D, max_blocks,
+        num_blocks, scale, _dt(q), _p(workspace), wbytes, _stream()))
+    return out
+
+
+def attn_adaptive_split(R, Hkv, max_blocks):
+    return _lib.biv_attn_adaptive_split(R, Hkv, max_blocks)
+
+
+def attn_decode_adaptive(q, k_cache, v_cache, block_table, ctx, out, q_len, scale, workspace, split_tokens=0):
+    _contig(k_cache, v_cache, block_table, ctx, out)
+    q_stride, Hq, D = _attn_checks(q, k_cache, v_cache, block_table, ctx, out, q_len)
+    R, max_blocks = block_table.shape
+    num_blocks, Hkv = k_cache.shape[0], k_cache.shape[1]
+    wbytes = workspace.numel() * workspace.element_size()
+    _check("attn_decode_adaptive", _lib.attn_decode_adaptive(
+        _p(q), q_stride, _p(k_cache), _p(v_cache), _p(block_table), _p(ctx), _p(out), R, q_len, Hq, Hkv, D, max_blocks,
+        num_blocks, scale, split_tokens, _p(workspace), wbytes, _stream()))
+    return out
+
+
+def gumbel_verify(logits, noise, cand, target, accept_len, next_token):
+    """logits/noise [R*K, V] fp32; cand/target [R, K] int32; accept_len/next_token [R] int32."""
+    _contig(logits, noise, cand, target, accept_len, next_token)
+    _want(logits, torch.float32, "logits")
+    _want(noise, torch.float32, "noise")
+    for t, n in ((cand, "cand"), (target, "target"), (accept_len, "accept_len"), (next_token, "next_token")):
+        _want(t, torch.int32, n)
+    R, K = cand.shape
+    V = logits.shape[-1]
+    assert logits.numel() == R * K * V and noise.numel() == R * K * V
+    assert target.numel() == R * K and accept_len.numel() == R and next_token.numel() == R
+    _check("gumbel_verify", _lib.gumbel_verify(_p(logits), _p(noise), _p(cand), R, K, V, _p(target),
+                                               _p(accept_len), _p(next_token), _stream()))
+    return target, accept_len, next_token
+
+
+def kv_overwrite(k_new, v_new, slot, k_cache, v_cache):
+    """k_new/v_new: [T, Hkv*D] views (row stride may exceed Hkv*D); slot [T] int64."""
+    T = slot.shape[0]
+    num_blocks, Hkv, _, D = k_cache.shape
+    _same_dtype(k_new, v_new, k_cache, v_cache)
+    _want(slot, torch.int64, "slot")
+    stride = k_new.stride(0)
+    assert v_new.stride(0) == stride and k_new.stride(-1) == 1 and v_new.stride(-1) == 1
+    assert tuple(k_new.shape) == (T, Hkv * D) and tuple(v_new.shape) == (T, Hkv * D)
+    assert k_cache.shape == v_cache.shape
+    _contig(slot, k_cache, v_cache)
+    _check("kv_overwrite", _lib.kv_overwrite(_p(k_new), _p(v_new), stride, _p(slot), _p(k_cache), _p(v_cache),
+                                             T, Hkv, D, num_blocks, _dt(k_cache), _stream()))
+
+
+def embed_rows(ids, table, out):
+    _contig(ids, table, out)
+    _want(ids, torch.int32, "ids")
+    V, H = table.shape
+    assert tuple(out.shape) == (ids.shape[0], H)
+    _check("embed_rows", _lib.embed_rows(_p(ids), _p(table), _dt(table), _p(out), _dt(out), ids.shape[0], V, H,
+                                         _stream()))
+    return out
+
+
+def rope_table(max_pos, D, theta):
+    """Host fp32 table [max_pos, D/2, 2] (cos, sin) made by the library."""
+    t = torch.empty((max_pos, D // 2, 2), dtype=torch.float32)
+    _check("biv_rope_table", _lib.biv_rope_table(ctypes.c_void_p(t.data_ptr()), max_pos, D, theta))
+    return t
+
+
+def rope_apply(x, pos, cos_sin, n_heads, D):
+    """In place on the first n_heads*D columns of each row of x (row stride x.stride(0))."""
+    assert x.stride(-1) == 1 and x.shape[1] >= n_heads * D
+    _contig(pos, cos_sin)
+    _want(pos, torch.int32, "pos")
+    _want(cos_sin, torch.float32, "cos_sin")
+    assert pos.numel() == x.shape[0] and cos_sin.shape[1] * 2 == D
+    _check("rope_apply", _lib.rope_apply(_p(x), x.stride(0), _p(pos), _p(cos_sin), x.shape[0], n_heads, D,
+                                         cos_sin.shape[0], _dt(x), _stream()))
+
+
+def swiglu(gu, out):
+    _contig(gu, out)
+    _same_dtype(gu, out)
+    M, N2 = gu.shape
+    assert tuple(out.shape) == (M, N2 // 2)
+    _check("swiglu", _lib.swiglu(_p(gu), _p(out), M, N2 // 2, _dt(gu), _stream()))
+    return out
+
+
+def splitk_workspace_bytes(M, N, splits):
+    return _lib.biv_splitk_workspace_bytes(M, N, splits)
+
+
+def splitk_auto_splits(M, N, K):
+    return _lib.biv_splitk_auto_splits(M, N, K)
+
+
+def gemm_splitk(a, b, c, splits, workspace, accumulate=False):
+    _contig(a, b, c, workspace)
+    _want(a, torch.bfloat16, "a")
+    _want(b, torch.bfloat16, "b")
+    M, K = a.shape
+    N = b.shape[0]
+    assert b.shape[1] == K and tuple(c.shape) == (M, N)
+    epi = BIV_EPI_ACCUM if accumulate else BIV_EPI_STORE
+    _check("gemm_splitk", _lib.gemm_splitk(_p(a), _p(b), _p(c), M, N, K, _dt(c), epi, splits, _p(workspace),
+                                           workspace.numel() * workspace.element_size(), _stream()))
+    return c
+
+
+def abi_version():
+    return _lib.biv_abi_version()

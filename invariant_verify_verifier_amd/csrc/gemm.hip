@@ -1,0 +1,318 @@
+// gemm_bi: batch-invariant matmul, and gemm_splitk, its non-invariant
+// split-K counterpart.
+//
+// LLM-42 post, paragraph 1: at small batch a matmul normally splits the
+// reduction dimension K into pieces computed in parallel and summed
+// afterwards (split-K); the batch-invariant matmul drops split-K and always
+// uses one and the same data-parallel tiling.
+//
+// bf16 path (gfx950 MFMA).  Workgroup tile 128 x 128 (M x N), K staged 64 at a
+// time through LDS (double buffered, 16-byte chunks XOR-swizzled by row so the
+// 128-bit fragment reads are bank-conflict free).  Four waves in a 2 x 2
+// arrangement each own 64 x 64 outputs as 2 x 2 blocks of the 32x32x16 bf16
+// MFMA.  Every output element is reduced by the same instruction over
+// k = 0, 16, 32, ... in ascending order with fp32 accumulators, so its bits
+// depend only on its own row of A and column of B: not on M, not on the tile
+// it lands in, not on the other rows.  The tiling is the same for every M.
+//
+// Workgroup -> tile mapping is XCD aware: the dispatcher deals workgroups to
+// the 8 XCDs round-robin, so workgroup b is remapped to give each XCD a
+// contiguous run of tiles, M-fastest, and the M tiles that share a B tile
+// meet in the same XCD's L2.
+#include <algorithm>
+
+#include "biv_internal.h"
+
+namespace biv {
+
+constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kGemmThreads = 256;
+constexpr int kTileBytes = kBM * kBK * 2;  // 16 KiB per operand tile
+
+// Byte offset of 16-byte chunk `chunk` (0..7) of row `row` in an LDS tile.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+
+__device__ __forceinline__ int xcd_remap(int b, int nb) {
+  const int per = nb >> 3;
+  return (b < (per << 3)) ? (b & 7) * per + (b >> 3) : b;
+}
+
+// kSplit: write fp32 partial sums of the K range [k_begin, k_end) to `partial`
+// ([split][M][N]) instead of running the epilogue.
+template <int OUT_DT, int EPI, bool kSplit>
+__global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
+                                                                 const uint16_t* __restrict__ B, void* C,
+                                                                 float* __restrict__ partial, int M, int N, int K,
+                                                                 int tilesM, int tilesN, int k_per_split) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2][2][kTileBytes];  // [buf][A/B]
+  const int tid = threadIdx.x;
+  const int logical = xcd_remap(blockIdx.x, tilesM * tilesN);
+  const int m0 = (logical % tilesM) * kBM;
+  const int n0 = (logical / tilesM) * kBN;
+  const int k_begin = kSplit ? blockIdx.y * k_per_split : 0;
+  const int k_end = kSplit ? min(K, k_begin + k_per_split) : K;
+
+  // global -> register staging: row = tid/8 + 32 i, chunk = tid % 8
+  const int lrow = tid >> 3, lch = tid & 7;
+  uint4 ra[4], rb[4];
+  auto load_tiles = [&](int k0) {
+    const int gk = k0 + lch * 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = lrow + 32 * i;
+      const int gm = m0 + row, gn = n0 + row;
+      ra[i] = (gm < M && gk < k_end) ? *reinterpret_cast<const uint4*>(A + (int64_t)gm * K + gk) : make_uint4(0, 0, 0, 0);
+      rb[i] = (gn < N && gk < k_end) ? *reinterpret_cast<const uint4*>(B + (int64_t)gn * K + gk) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_tiles = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = lrow + 32 * i;
+      *reinterpret_cast<uint4*>(&smem[buf][0][swz(row, lch)]) = ra[i];
+      *reinterpret_cast<uint4*>(&smem[buf][1][swz(row, lch)]) = rb[i];
+    }
+  };
+
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int g = lane >> 5, li = lane & 31;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const int nk = (int)cdiv(k_end - k_begin, kBK);
+  load_tiles(k_begin);
+  store_tiles(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load_tiles(k_begin + (kt + 1) * kBK);
+    const unsigned char* As = smem[cur][0];
+    const unsigned char* Bs = smem[cur][1];
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      const int chunk = 2 * ks + g;  // lanes 0-31 take k 0..7 of the step, lanes 32-63 k 8..15
+      bf16x8 a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) a[i] = *reinterpret_cast<const bf16x8*>(As + swz(64 * wm + 32 * i + li, chunk));
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b[j] = *reinterpret_cast<const bf16x8*>(Bs + swz(64 * wn + 32 * j + li, chunk));
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) store_tiles(cur ^ 1);
+    __syncthreads();
+  }
+
+  // 32x32 accumulator layout: lane holds column li; value v is row 8(v/4) + 4g + v%4.
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + 64 * wn + 32 * j + li;
+      if (n >= N) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = m0 + 64 * wm + 32 * i + 8 * (v >> 2) + 4 * g + (v & 3);
+        if (m >= M) continue;
+        const int64_t idx = (int64_t)m * N + n;
+        const float x = acc[i][j][v];
+        if (kSplit) {
+          partial[(int64_t)blockIdx.y * M * N + idx] = x;
+        } else if (EPI == BIV_EPI_ACCUM) {
+          store_from_f32(C, idx, __fadd_rn(load_as_f32(C, idx, OUT_DT), x), OUT_DT);
+        } else {
+          store_from_f32(C, idx, x, OUT_DT);
+        }
+      }
+    }
+}
+
+// fp32 path: 64 x 64 tiles, K staged 16 at a time, each lane owns 4 x 4
+// outputs; every output is one fused multiply-add chain over k ascending.
+constexpr int kFT = 64, kFK = 16;
+
+template <int OUT_DT, int EPI>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A, const float* __restrict__ B,
+                                                       void* C, int M, int N, int K) {
+  __shared__ float As[kFK][kFT + 4];
+  __shared__ float Bs[kFK][kFT + 4];
+  const int tid = threadIdx.x;
+  const int tx = tid & 15, ty = tid >> 4;
+  const int m0 = blockIdx.y * kFT, n0 = blockIdx.x * kFT;
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+  for (int k0 = 0; k0 < K; k0 += kFK) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = tid + 256 * e;
+      const int row = idx >> 4, kk = idx & 15;
+      const int gk = k0 + kk;
+      As[kk][row] = (m0 + row < M && gk < K) ? A[(int64_t)(m0 + row) * K + gk] : 0.0f;
+      Bs[kk][row] = (n0 + row < N && gk < K) ? B[(int64_t)(n0 + row) * K + gk] : 0.0f;
+    }
+    __syncthreads();
+    const int kmax = min(kFK, K - k0);
+    for (int kk = 0; kk < kmax; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __fmaf_rn(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + ty * 4 + i;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tx * 4 + j;
+      if (n >= N) continue;
+      const int64_t idx = (int64_t)m * N + n;
+      if (EPI == BIV_EPI_ACCUM)
+        store_from_f32(C, idx, __fadd_rn(load_as_f32(C, idx, OUT_DT), acc[i][j]), OUT_DT);
+      else
+        store_from_f32(C, idx, acc[i][j], OUT_DT);
+    }
+  }
+}
+
+// Split-K second pass: C = sum over splits (ascending) of the partials.
+template <int OUT_DT, int EPI>
+__global__ void splitk_reduce_kernel(const float* __restrict__ partial, void* C, int64_t MN, int splits) {
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < MN; e += (int64_t)gridDim.x * blockDim.x) {
+    float s = partial[e];
+    for (int k = 1; k < splits; ++k) s = __fadd_rn(s, partial[(int64_t)k * MN + e]);
+    if (EPI == BIV_EPI_ACCUM) s = __fadd_rn(load_as_f32(C, e, OUT_DT), s);
+    store_from_f32(C, e, s, OUT_DT);
+  }
+}
+
+template <int OUT_DT, int EPI, bool kSplit>
+static void launch_bf16(const void* A, const void* B, void* C, float* partial, int M, int N, int K, int splits,
+                        int k_per_split, hipStream_t s) {
+  const int tilesM = (int)cdiv(M, kBM), tilesN = (int)cdiv(N, kBN);
+  hipLaunchKernelGGL((gemm_bf16_kernel<OUT_DT, EPI, kSplit>), dim3(tilesM * tilesN, splits), dim3(kGemmThreads), 0,
+                     s, static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), C, partial, M, N, K,
+                     tilesM, tilesN, k_per_split);
+}
+
+static biv_status check_gemm_args(const char* who, const void* A, const void* B, void* C, int64_t M, int64_t N,
+                                  int64_t K, int out_dt, int epilogue) {
+  BIV_REQUIRE(valid_dt(out_dt), "%s: bad out dtype %d", who, out_dt);
+  BIV_REQUIRE(epilogue == BIV_EPI_STORE || epilogue == BIV_EPI_ACCUM, "%s: bad epilogue %d", who, epilogue);
+  BIV_REQUIRE(M >= 0 && N >= 1 && K >= 1, "%s: bad sizes M=%lld N=%lld K=%lld", who, (long long)M, (long long)N,
+              (long long)K);
+  BIV_REQUIRE(M <= (1 << 30) && N <= (1 << 30) && K <= (1 << 30), "%s: size too large", who);
+  if (M > 0) BIV_REQUIRE(A && B && C, "%s: NULL pointer", who);
+  return BIV_OK;
+}
+
+}  // namespace biv
+
+extern "C" biv_status gemm_bi(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                              biv_dtype in_dt, biv_dtype out_dt, int epilogue, biv_stream stream) {
+  using namespace biv;
+  BIV_REQUIRE(valid_dt(in_dt), "gemm_bi: bad in dtype %d", (int)in_dt);
+  biv_status st = check_gemm_args("gemm_bi", A, B, C, M, N, K, out_dt, epilogue);
+  if (st != BIV_OK) return st;
+  if (M == 0) return BIV_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int m = (int)M, n = (int)N, k = (int)K;
+  if (in_dt == BIV_BF16) {
+    BIV_REQUIRE(K % 8 == 0, "gemm_bi: bf16 path needs K %% 8 == 0 (K=%lld)", (long long)K);
+    BIV_REQUIRE(aligned16(A) && aligned16(B), "gemm_bi: bf16 path needs 16-byte aligned A and B");
+    BIV_REQUIRE(cdiv(M, kBM) * cdiv(N, kBN) <= 0x7fffffff, "gemm_bi: too many tiles");
+    if (out_dt == BIV_BF16) {
+      if (epilogue == BIV_EPI_ACCUM) launch_bf16<BIV_BF16, BIV_EPI_ACCUM, false>(A, B, C, nullptr, m, n, k, 1, k, s);
+      else launch_bf16<BIV_BF16, BIV_EPI_STORE, false>(A, B, C, nullptr, m, n, k, 1, k, s);
+    } else {
+      if (epilogue == BIV_EPI_ACCUM) launch_bf16<BIV_F32, BIV_EPI_ACCUM, false>(A, B, C, nullptr, m, n, k, 1, k, s);
+      else launch_bf16<BIV_F32, BIV_EPI_STORE, false>(A, B, C, nullptr, m, n, k, 1, k, s);
+    }
+    return launched("gemm_bi/bf16");
+  }
+  dim3 grid((unsigned)cdiv(N, kFT), (unsigned)cdiv(M, kFT));
+  BIV_REQUIRE(cdiv(M, kFT) <= 65535, "gemm_bi: fp32 path supports M <= %d", 65535 * kFT);
+  const float* a = static_cast<const float*>(A);
+  const float* b = static_cast<const float*>(B);
+  if (out_dt == BIV_F32) {
+    if (epilogue == BIV_EPI_ACCUM) hipLaunchKernelGGL((gemm_f32_kernel<BIV_F32, BIV_EPI_ACCUM>), grid, dim3(256), 0, s, a, b, C, m, n, k);
+    else hipLaunchKernelGGL((gemm_f32_kernel<BIV_F32, BIV_EPI_STORE>), grid, dim3(256), 0, s, a, b, C, m, n, k);
+  } else {
+    if (epilogue == BIV_EPI_ACCUM) hipLaunchKernelGGL((gemm_f32_kernel<BIV_BF16, BIV_EPI_ACCUM>), grid, dim3(256), 0, s, a, b, C, m, n, k);
+    else hipLaunchKernelGGL((gemm_f32_kernel<BIV_BF16, BIV_EPI_STORE>), grid, dim3(256), 0, s, a, b, C, m, n, k);
+  }
+  return launched("gemm_bi/f32");
+}
+
+namespace biv {
+// Split count chosen the way a throughput-oriented library would: enough
+// workgroups for two per compute unit, each split at least two K tiles.
+static int auto_splits(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = cdiv(M, kBM) * cdiv(N, kBN);
+  int64_t s = cdiv(512, tiles);
+  s = std::min<int64_t>(s, std::max<int64_t>(1, K / (2 * kBK)));
+  return (int)std::max<int64_t>(1, std::min<int64_t>(s, 64));
+}
+static int split_len(int64_t K, int splits) { return (int)(cdiv(cdiv(K, splits), kBK) * kBK); }
+}  // namespace biv
+
+extern "C" int biv_splitk_auto_splits(int64_t M, int64_t N, int64_t K) {
+  using namespace biv;
+  if (M <= 0 || N <= 0 || K <= 0) return 1;
+  const int sp = auto_splits(M, N, K);
+  return (int)cdiv(K, split_len(K, sp));
+}
+
+extern "C" size_t biv_splitk_workspace_bytes(int64_t M, int64_t N, int splits) {
+  if (M <= 0 || N <= 0 || splits < 1) return 0;
+  return (size_t)splits * (size_t)M * (size_t)N * sizeof(float);
+}
+
+extern "C" biv_status gemm_splitk(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                                  biv_dtype out_dt, int epilogue, int splits, void* workspace,
+                                  size_t workspace_bytes, biv_stream stream) {
+  using namespace biv;
+  biv_status st = check_gemm_args("gemm_splitk", A, B, C, M, N, K, out_dt, epilogue);
+  if (st != BIV_OK) return st;
+  BIV_REQUIRE(splits >= 0 && splits <= 64, "gemm_splitk: splits must be in [0, 64]");
+  if (M == 0) return BIV_OK;
+  BIV_REQUIRE(K % 8 == 0 && aligned16(A) && aligned16(B), "gemm_splitk: needs K %% 8 == 0 and aligned A, B");
+  int sp = splits == 0 ? auto_splits(M, N, K) : splits;
+  const int kps = split_len(K, sp);
+  sp = (int)cdiv(K, kps);  // drop empty splits
+  BIV_REQUIRE(workspace != nullptr && workspace_bytes >= biv_splitk_workspace_bytes(M, N, sp),
+              "gemm_splitk: workspace needs %zu bytes", biv_splitk_workspace_bytes(M, N, sp));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* part = static_cast<float*>(workspace);
+  launch_bf16<BIV_F32, BIV_EPI_STORE, true>(A, B, C, part, (int)M, (int)N, (int)K, sp, kps, s);
+  st = launched("gemm_splitk/partials");
+  if (st != BIV_OK) return st;
+  const int64_t MN = M * N;
+  const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(MN, 256), 16384);
+  if (out_dt == BIV_BF16) {
+    if (epilogue == BIV_EPI_ACCUM) hipLaunchKernelGGL((splitk_reduce_kernel<BIV_BF16, BIV_EPI_ACCUM>), dim3(blocks), dim3(256), 0, s, part, C, MN, sp);
+    else hipLaunchKernelGGL((splitk_reduce_kernel<BIV_BF16, BIV_EPI_STORE>), dim3(blocks), dim3(256), 0, s, part, C, MN, sp);
+  } else {
+    if (epilogue == BIV_EPI_ACCUM) hipLaunchKernelGGL((splitk_reduce_kernel<BIV_F32, BIV_EPI_ACCUM>), dim3(blocks), dim3(256), 0, s, part, C, MN, sp);
+    else hipLaunchKernelGGL((splitk_reduce_kernel<BIV_F32, BIV_EPI_STORE>), dim3(blocks), dim3(256), 0, s, part, C, MN, sp);
+  }
+  return launched("gemm_splitk/reduce");
+}

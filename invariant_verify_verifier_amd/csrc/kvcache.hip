@@ -1,0 +1,172 @@
+// kv_overwrite and the row-local elementwise helpers of the decoder forward.
+//
+// kv_overwrite follows the LLM-42 post, paragraph 3: the fast path's KV was
+// computed at some other batch size and would pass its numerical drift on to
+// later forwards, so every verification overwrites those slots with the
+// verifier's values.  It is a bit copy into a paged cache
+// [num_blocks, Hkv, 16, D]; one thread moves 16 bytes.
+#include "biv_internal.h"
+
+namespace biv {
+
+// One 16-byte piece per thread: piece p of token t, head h.
+__global__ void kv_overwrite_vec_kernel(const uint4* __restrict__ k_new, const uint4* __restrict__ v_new,
+                                        int64_t src_stride16, const int64_t* __restrict__ slot,
+                                        uint4* __restrict__ k_cache, uint4* __restrict__ v_cache, int T,
+                                        int Hkv, int row16, int64_t num_slots) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_tok = (int64_t)Hkv * row16;
+  if (gid >= (int64_t)T * per_tok) return;
+  const int t = (int)(gid / per_tok);
+  const int64_t rem = gid - (int64_t)t * per_tok;  // h * row16 + piece
+  const int h = (int)(rem / row16);
+  const int piece = (int)(rem - (int64_t)h * row16);
+  const int64_t s = slot[t];
+  if (s < 0 || s >= num_slots) return;
+  const int64_t page = s >> 4, off = s & 15;
+  const int64_t dst = ((page * Hkv + h) * 16 + off) * row16 + piece;
+  const int64_t src = (int64_t)t * src_stride16 + rem;
+  k_cache[dst] = k_new[src];
+  v_cache[dst] = v_new[src];
+}
+
+// Element-wise fallback for unaligned rows.
+template <typename E>
+__global__ void kv_overwrite_elem_kernel(const E* __restrict__ k_new, const E* __restrict__ v_new,
+                                         int64_t src_stride, const int64_t* __restrict__ slot,
+                                         E* __restrict__ k_cache, E* __restrict__ v_cache, int T, int Hkv, int D,
+                                         int64_t num_slots) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_tok = (int64_t)Hkv * D;
+  if (gid >= (int64_t)T * per_tok) return;
+  const int t = (int)(gid / per_tok);
+  const int64_t rem = gid - (int64_t)t * per_tok;
+  const int h = (int)(rem / D);
+  const int d = (int)(rem - (int64_t)h * D);
+  const int64_t s = slot[t];
+  if (s < 0 || s >= num_slots) return;
+  const int64_t dst = (((s >> 4) * Hkv + h) * 16 + (s & 15)) * D + d;
+  k_cache[dst] = k_new[(int64_t)t * src_stride + rem];
+  v_cache[dst] = v_new[(int64_t)t * src_stride + rem];
+}
+
+__global__ void embed_rows_kernel(const int32_t* __restrict__ ids, const void* __restrict__ table, int table_dt,
+                                  void* __restrict__ out, int out_dt, int V, int H) {
+  const int t = blockIdx.x;
+  const int id = ids[t];
+  const bool ok = id >= 0 && id < V;
+  for (int i = threadIdx.x; i < H; i += blockDim.x) {
+    const float v = ok ? load_as_f32(table, (int64_t)id * H + i, table_dt) : 0.0f;
+    store_from_f32(out, (int64_t)t * H + i, v, out_dt);
+  }
+}
+
+// One thread per (token, head, pair i < D/2).
+__global__ void rope_apply_kernel(void* __restrict__ x, int64_t stride, const int32_t* __restrict__ pos,
+                                  const float* __restrict__ cos_sin, int T, int n_heads, int D, int max_pos,
+                                  int dt) {
+  const int half = D >> 1;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)T * n_heads * half) return;
+  const int t = (int)(gid / ((int64_t)n_heads * half));
+  const int rem = (int)(gid - (int64_t)t * n_heads * half);
+  const int h = rem / half, i = rem - h * half;
+  const int p = pos[t];
+  if (p < 0 || p >= max_pos) return;
+  const float c = cos_sin[((int64_t)p * half + i) * 2 + 0];
+  const float s = cos_sin[((int64_t)p * half + i) * 2 + 1];
+  const int64_t ia = (int64_t)t * stride + (int64_t)h * D + i;
+  const int64_t ib = ia + half;
+  const float a = load_as_f32(x, ia, dt), b = load_as_f32(x, ib, dt);
+  const float ra = __fsub_rn(__fmul_rn(a, c), __fmul_rn(b, s));
+  const float rb = __fadd_rn(__fmul_rn(b, c), __fmul_rn(a, s));
+  store_from_f32(x, ia, ra, dt);
+  store_from_f32(x, ib, rb, dt);
+}
+
+__global__ void swiglu_kernel(const void* __restrict__ gu, void* __restrict__ out, int64_t M, int64_t N, int dt) {
+  const int64_t total = M * N;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = e / N, n = e - m * N;
+    const float g = load_as_f32(gu, m * 2 * N + n, dt);
+    const float u = load_as_f32(gu, m * 2 * N + N + n, dt);
+    const float act = __fdiv_rn(g, __fadd_rn(1.0f, expf(-g)));
+    store_from_f32(out, e, __fmul_rn(act, u), dt);
+  }
+}
+
+}  // namespace biv
+
+extern "C" biv_status kv_overwrite(const void* k_new, const void* v_new, int64_t src_stride, const int64_t* slot,
+                                   void* k_cache, void* v_cache, int T, int Hkv, int D, int num_blocks,
+                                   biv_dtype dt, biv_stream stream) {
+  using namespace biv;
+  BIV_REQUIRE(valid_dt(dt), "kv_overwrite: bad dtype %d", (int)dt);
+  BIV_REQUIRE(T >= 0 && Hkv >= 1 && D >= 1 && num_blocks >= 0, "kv_overwrite: bad sizes T=%d Hkv=%d D=%d", T, Hkv, D);
+  BIV_REQUIRE(src_stride >= (int64_t)Hkv * D, "kv_overwrite: src_stride %lld < Hkv*D", (long long)src_stride);
+  if (T == 0) return BIV_OK;
+  BIV_REQUIRE(k_new && v_new && slot && k_cache && v_cache, "kv_overwrite: NULL pointer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t es = dt_size(dt);
+  const int64_t num_slots = (int64_t)num_blocks * 16;
+  const bool vec = ((size_t)D * es) % 16 == 0 && ((size_t)src_stride * es) % 16 == 0 && aligned16(k_new) &&
+                   aligned16(v_new) && aligned16(k_cache) && aligned16(v_cache);
+  if (vec) {
+    const int row16 = (int)((size_t)D * es / 16);
+    const int64_t n = (int64_t)T * Hkv * row16;
+    hipLaunchKernelGGL(kv_overwrite_vec_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s,
+                       static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new),
+                       (int64_t)((size_t)src_stride * es / 16), slot, static_cast<uint4*>(k_cache),
+                       static_cast<uint4*>(v_cache), T, Hkv, row16, num_slots);
+  } else {
+    const int64_t n = (int64_t)T * Hkv * D;
+    if (dt == BIV_BF16)
+      hipLaunchKernelGGL(kv_overwrite_elem_kernel<uint16_t>, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s,
+                         static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), src_stride, slot,
+                         static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), T, Hkv, D, num_slots);
+    else
+      hipLaunchKernelGGL(kv_overwrite_elem_kernel<float>, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s,
+                         static_cast<const float*>(k_new), static_cast<const float*>(v_new), src_stride, slot,
+                         static_cast<float*>(k_cache), static_cast<float*>(v_cache), T, Hkv, D, num_slots);
+  }
+  return launched("kv_overwrite");
+}
+
+extern "C" biv_status embed_rows(const int32_t* ids, const void* table, biv_dtype table_dt, void* out,
+                                 biv_dtype out_dt, int T, int V, int H, biv_stream stream) {
+  using namespace biv;
+  BIV_REQUIRE(valid_dt(table_dt) && valid_dt(out_dt), "embed_rows: bad dtype");
+  BIV_REQUIRE(T >= 0 && V >= 1 && H >= 1, "embed_rows: bad sizes");
+  if (T == 0) return BIV_OK;
+  BIV_REQUIRE(ids && table && out, "embed_rows: NULL pointer");
+  hipLaunchKernelGGL(embed_rows_kernel, dim3(T), dim3(256), 0, static_cast<hipStream_t>(stream), ids, table,
+                     (int)table_dt, out, (int)out_dt, V, H);
+  return launched("embed_rows");
+}
+
+extern "C" biv_status rope_apply(void* x, int64_t stride, const int32_t* pos, const float* cos_sin, int T,
+                                 int n_heads, int D, int max_pos, biv_dtype dt, biv_stream stream) {
+  using namespace biv;
+  BIV_REQUIRE(valid_dt(dt), "rope_apply: bad dtype");
+  BIV_REQUIRE(T >= 0 && n_heads >= 1 && D >= 2 && D % 2 == 0 && max_pos >= 1, "rope_apply: bad sizes");
+  BIV_REQUIRE(stride >= (int64_t)n_heads * D, "rope_apply: stride < n_heads*D");
+  if (T == 0) return BIV_OK;
+  BIV_REQUIRE(x && pos && cos_sin, "rope_apply: NULL pointer");
+  const int64_t n = (int64_t)T * n_heads * (D / 2);
+  hipLaunchKernelGGL(rope_apply_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), x, stride, pos, cos_sin, T, n_heads, D, max_pos, (int)dt);
+  return launched("rope_apply");
+}
+
+extern "C" biv_status swiglu(const void* gu, void* out, int64_t M, int64_t N, biv_dtype dt, biv_stream stream) {
+  using namespace biv;
+  BIV_REQUIRE(valid_dt(dt), "swiglu: bad dtype");
+  BIV_REQUIRE(M >= 0 && N >= 1, "swiglu: bad sizes");
+  if (M == 0) return BIV_OK;
+  BIV_REQUIRE(gu && out, "swiglu: NULL pointer");
+  const int64_t n = M * N;
+  const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(n, 256), 8192);
+  hipLaunchKernelGGL(swiglu_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), gu, out, M, N,
+                     (int)dt);
+  return launched("swiglu");
+}

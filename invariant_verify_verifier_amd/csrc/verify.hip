@@ -1,0 +1,130 @@
+// gumbel_verify: Gumbel-max coupled verification of K candidates per request.
+//
+// Reading-club post on Gumbel coupling: the Gumbel-max trick samples from the
+// softmax as argmax(logits + g) with g ~ Gumbel(0,1) prepared in advance;
+// with the same noise on both sides, verification reduces to comparing the
+// draft's token with the target's token.
+//
+// Kernel 1 (one workgroup per row r*K + j): stream the row's logits and noise
+// (HBM-bound, 8 bytes per vocab entry), s = fl32(l + g), keep the best
+// (value, index) pair per lane, reduce across the workgroup.  The pair order
+// "larger value wins, equal values go to the lower index" is associative and
+// commutative, so the reduction order cannot change the result.
+// Kernel 2 (one lane per request): first j with target != cand.
+#include "biv_internal.h"
+
+namespace biv {
+
+constexpr int kVerifyThreads = 1024;
+
+__device__ __forceinline__ void take_better(float& bv, int& bi, float v, int i) {
+  v = (v != v) ? -INFINITY : v;  // NaN never wins
+  if (v > bv || (v == bv && i < bi)) {
+    bv = v;
+    bi = i;
+  }
+}
+
+template <bool kVec4>
+__global__ __launch_bounds__(kVerifyThreads) void gumbel_argmax_kernel(const float* __restrict__ logits,
+                                                                       const float* __restrict__ noise,
+                                                                       int V, int32_t* __restrict__ target) {
+  const int64_t row = blockIdx.x;
+  const float* lr = logits + row * (int64_t)V;
+  const float* nr = noise + row * (int64_t)V;
+  float bv = -INFINITY;
+  int bi = V;  // loses every comparison with a real index
+  if (kVec4) {
+    const f32x4* l4 = reinterpret_cast<const f32x4*>(lr);
+    const f32x4* n4 = reinterpret_cast<const f32x4*>(nr);
+    const int V4 = V >> 2;
+    int i = threadIdx.x;
+    // four independent 32-byte pairs in flight per lane
+    for (; i + 3 * kVerifyThreads < V4; i += 4 * kVerifyThreads) {
+      f32x4 a[4], b[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        a[u] = __builtin_nontemporal_load(l4 + i + u * kVerifyThreads);
+        b[u] = __builtin_nontemporal_load(n4 + i + u * kVerifyThreads);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int base = 4 * (i + u * kVerifyThreads);
+        take_better(bv, bi, a[u].x + b[u].x, base + 0);
+        take_better(bv, bi, a[u].y + b[u].y, base + 1);
+        take_better(bv, bi, a[u].z + b[u].z, base + 2);
+        take_better(bv, bi, a[u].w + b[u].w, base + 3);
+      }
+    }
+    for (; i < V4; i += kVerifyThreads) {
+      const f32x4 a = __builtin_nontemporal_load(l4 + i);
+      const f32x4 b = __builtin_nontemporal_load(n4 + i);
+      take_better(bv, bi, a.x + b.x, 4 * i + 0);
+      take_better(bv, bi, a.y + b.y, 4 * i + 1);
+      take_better(bv, bi, a.z + b.z, 4 * i + 2);
+      take_better(bv, bi, a.w + b.w, 4 * i + 3);
+    }
+  } else {
+    for (int i = threadIdx.x; i < V; i += kVerifyThreads) take_better(bv, bi, lr[i] + nr[i], i);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float ov = __shfl_xor(bv, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    take_better(bv, bi, ov, oi);
+  }
+  __shared__ float sv[kVerifyThreads / 64];
+  __shared__ int si[kVerifyThreads / 64];
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sv[wave] = bv;
+    si[wave] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kVerifyThreads / 64; ++w) take_better(bv, bi, sv[w], si[w]);
+    target[row] = bi;
+  }
+}
+
+__global__ void verify_decide_kernel(const int32_t* __restrict__ target, const int32_t* __restrict__ cand,
+                                     int R, int K, int32_t* __restrict__ accept_len,
+                                     int32_t* __restrict__ next_token) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= R) return;
+  int a = K, nx = -1;
+  for (int j = 0; j < K; ++j) {
+    const int t = target[(int64_t)r * K + j];
+    if (t != cand[(int64_t)r * K + j]) {
+      a = j;
+      nx = t;
+      break;
+    }
+  }
+  accept_len[r] = a;
+  next_token[r] = nx;
+}
+
+}  // namespace biv
+
+extern "C" biv_status gumbel_verify(const float* logits, const float* noise, const int32_t* cand, int R,
+                                    int K, int V, int32_t* target, int32_t* accept_len,
+                                    int32_t* next_token, biv_stream stream) {
+  using namespace biv;
+  BIV_REQUIRE(R >= 0 && K >= 1 && V >= 1, "gumbel_verify: need R >= 0, K >= 1, V >= 1 (R=%d K=%d V=%d)", R, K, V);
+  BIV_REQUIRE((int64_t)R * K <= 0x7fffffff, "gumbel_verify: R*K too large");
+  if (R == 0) return BIV_OK;
+  BIV_REQUIRE(logits && noise && cand && target && accept_len && next_token, "gumbel_verify: NULL pointer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool vec = (V % 4 == 0) && aligned16(logits) && aligned16(noise);
+  const unsigned rows = (unsigned)(R * K);
+  if (vec)
+    hipLaunchKernelGGL(gumbel_argmax_kernel<true>, dim3(rows), dim3(kVerifyThreads), 0, s, logits, noise, V, target);
+  else
+    hipLaunchKernelGGL(gumbel_argmax_kernel<false>, dim3(rows), dim3(kVerifyThreads), 0, s, logits, noise, V, target);
+  biv_status st = launched("gumbel_verify/argmax");
+  if (st != BIV_OK) return st;
+  hipLaunchKernelGGL(verify_decide_kernel, dim3((R + 63) / 64), dim3(64), 0, s, target, cand, R, K, accept_len,
+                     next_token);
+  return launched("gumbel_verify/decide");
+}

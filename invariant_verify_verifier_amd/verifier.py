@@ -1,0 +1,253 @@
+"""The verifier step: decoder forward over W = N*K candidate tokens, Gumbel-max
+verification and the rollback rule.
+
+LLM-42 post, paragraph 3: the fast path decodes with ordinary kernels and
+produces candidate tokens; the verifier -- a forward at a fixed batch, the
+ground truth -- checks them, starting from the last token known to be
+correct, and at every verification overwrites the fast path's KV with its own
+values.  Paragraph 4: the verifier takes K tokens from each of N requests, so
+W = N*K is both its batch and the number of tokens it checks.  The reading-club
+post on Gumbel coupling gives the check itself: with the noise shared between
+draft and target, accept while the tokens agree.
+
+This module only sequences library calls and owns device buffers; every
+arithmetic step runs in libbiverify's kernels.  Inputs for request r are
+[t0_r, c_0, .., c_{K-2}] at positions L_r .. L_r+K-1; output j predicts
+position L_r + j + 1 and is compared with c_j.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+
+@dataclass
+class Shape:
+    layers: int
+    hidden: int
+    heads: int
+    kv_heads: int
+    head_dim: int
+    ffn: int
+    vocab: int
+    eps: float = 1e-6
+    rope_theta: float = 500000.0
+
+    @property
+    def q_cols(self):
+        return self.heads * self.head_dim
+
+    @property
+    def kv_cols(self):
+        return self.kv_heads * self.head_dim
+
+    @property
+    def qkv_cols(self):
+        return self.q_cols + 2 * self.kv_cols
+
+
+def _t(a, dtype, device):
+    """numpy input (fp32 values or bf16 bit patterns) -> device tensor."""
+    a = np.ascontiguousarray(a)
+    if dtype == torch.bfloat16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(a.astype(np.float32)).to(device)
+
+
+class VerifierModel:
+    """Decoder weights on the GPU and the verifier forward.
+
+    Weight layout [out_features, in_features]; Q, K, V projections fused into
+    one [Hq*D + 2*Hkv*D, H] matrix and gate/up into one [2F, H] matrix, so one
+    GEMM produces each.  The residual stream is fp32; GEMM inputs are the
+    model dtype (bf16: MFMA; fp32: FMA path).
+    """
+
+    def __init__(self, shape: Shape, dtype: torch.dtype, layers, embed, lm_head, final_norm, max_pos=65536,
+                 device="cuda"):
+        self.shape, self.dtype, self.device = shape, dtype, device
+        self.layers, self.embed, self.lm_head, self.final_norm = layers, embed, lm_head, final_norm
+        self.max_pos = max_pos
+        self.rope = L.rope_table(max_pos, shape.head_dim, shape.rope_theta).to(device)
+        self._bufs = {}
+        self._ws = {}
+
+    # ------------------------------------------------------------ construction
+
+    @classmethod
+    def from_host(cls, w, device="cuda", max_pos=65536):
+        """From workloads.ModelWeights (numpy; fp32 values or bf16 bits)."""
+        s = w.shape
+        shape = Shape(s.layers if not w.layers else len(w.layers), s.hidden, s.heads, s.kv_heads, s.head_dim, s.ffn,
+                      s.vocab, s.eps, s.rope_theta)
+        dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        layers = []
+        for lw in w.layers:
+            layers.append(dict(
+                attn_norm=_t(lw["attn_norm"], dt, device),
+                wqkv=_t(np.concatenate([lw["wq"], lw["wk"], lw["wv"]], axis=0), dt, device),
+                wo=_t(lw["wo"], dt, device),
+                ffn_norm=_t(lw["ffn_norm"], dt, device),
+                w_gu=_t(np.concatenate([lw["w_gate"], lw["w_up"]], axis=0), dt, device),
+                w_down=_t(lw["w_down"], dt, device),
+            ))
+        return cls(shape, dt, layers, _t(w.embed, dt, device), _t(w.lm_head, dt, device),
+                   _t(w.final_norm, dt, device), max_pos=max_pos, device=device)
+
+    def alloc_kv(self, num_blocks, fill=None):
+        sh = self.shape
+        caches = []
+        for _ in range(sh.layers):
+            k = torch.zeros((num_blocks, sh.kv_heads, 16, sh.head_dim), dtype=self.dtype, device=self.device)
+            v = torch.zeros_like(k)
+            caches.append((k, v))
+        return caches
+
+    # ------------------------------------------------------------ buffers
+
+    def _buffers(self, W):
+        b = self._bufs.get(W)
+        if b is None:
+            sh, dt, dev = self.shape, self.dtype, self.device
+            b = dict(
+                x=torch.empty((W, sh.hidden), dtype=torch.float32, device=dev),
+                h=torch.empty((W, sh.hidden), dtype=dt, device=dev),
+                qkv=torch.empty((W, sh.qkv_cols), dtype=dt, device=dev),
+                attn=torch.empty((W, sh.heads, sh.head_dim), dtype=dt, device=dev),
+                gu=torch.empty((W, 2 * sh.ffn), dtype=dt, device=dev),
+                act=torch.empty((W, sh.ffn), dtype=dt, device=dev),
+                logits=torch.empty((W, sh.vocab), dtype=torch.float32, device=dev),
+            )
+            self._bufs[W] = b
+        return b
+
+    def workspace(self, R, max_blocks):
+        key = (R, max_blocks)
+        ws = self._ws.get(key)
+        if ws is None:
+            nbytes = L.attn_workspace_bytes(R, self.shape.kv_heads, max_blocks)
+            ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=self.device)
+            self._ws[key] = ws
+        return ws
+
+    # ------------------------------------------------------------ forward
+
+    def forward(self, tokens, pos, ctx, q_len, block_table, slots, caches, attn_fn=None, gemm_fn=None):
+        """tokens/pos [W] int32, ctx [R] int32, block_table [R, mb] int32, slots [W] int64 (device).
+        Returns fp32 logits [W, V] (a buffer reused by the next call with the same W)."""
+        sh = self.shape
+        W = tokens.shape[0]
+        R, mb = block_table.shape
+        b = self._buffers(W)
+        x, h, qkv, attn, gu, act, logits = b["x"], b["h"], b["qkv"], b["attn"], b["gu"], b["act"], b["logits"]
+        ws = self.workspace(R, mb) if self.dtype == torch.bfloat16 else None
+        scale = 1.0 / math.sqrt(sh.head_dim)
+        gemm = gemm_fn or L.gemm_bi
+        attend = attn_fn or L.attn_decode_bi
+        qc, kc = sh.q_cols, sh.kv_cols
+        L.embed_rows(tokens, self.embed, x)
+        for li, lw in enumerate(self.layers):
+            k_cache, v_cache = caches[li]
+            L.rmsnorm_bi(x, lw["attn_norm"], h, sh.eps)
+            gemm(h, lw["wqkv"], qkv)
+            L.rope_apply(qkv, pos, self.rope, sh.heads + sh.kv_heads, sh.head_dim)
+            L.kv_overwrite(qkv[:, qc:qc + kc], qkv[:, qc + kc:], slots, k_cache, v_cache)
+            attend(qkv[:, :qc], k_cache, v_cache, block_table, ctx, attn, q_len, scale, ws)
+            gemm(attn.view(W, qc), lw["wo"], x, accumulate=True)
+            L.rmsnorm_bi(x, lw["ffn_norm"], h, sh.eps)
+            gemm(h, lw["w_gu"], gu)
+            L.swiglu(gu, act)
+            gemm(act, lw["w_down"], x, accumulate=True)
+        L.rmsnorm_bi(x, self.final_norm, h, sh.eps)
+        gemm(h, self.lm_head, logits)
+        return logits
+
+    def verify(self, step, caches, **kw):
+        """One verifier step.  `step` is a VerifyBatch already on the device.
+        Returns (logits [W,V], target [R,K], accept_len [R], next_token [R])."""
+        logits = self.forward(step.tokens, step.pos, step.ctx, step.K, step.block_table, step.slots, caches, **kw)
+        L.gumbel_verify(logits, step.noise, step.cand, step.target, step.accept_len, step.next_token)
+        return logits, step.target, step.accept_len, step.next_token
+
+
+@dataclass
+class VerifyBatch:
+    """Device inputs/outputs of one verifier step for R requests x K candidates."""
+
+    K: int
+    tokens: torch.Tensor  # [R*K] int32: t0, c_0 .. c_{K-2}
+    pos: torch.Tensor  # [R*K] int32: L_r + j
+    ctx: torch.Tensor  # [R] int32: L_r
+    block_table: torch.Tensor  # [R, max_blocks] int32
+    slots: torch.Tensor  # [R*K] int64: physical slot of position L_r + j
+    cand: torch.Tensor  # [R, K] int32
+    noise: torch.Tensor  # [R*K, V] fp32: noise of position L_r + j + 1
+    target: torch.Tensor
+    accept_len: torch.Tensor
+    next_token: torch.Tensor
+
+
+def make_batch(t0, cand, ctx, block_table, noise, device="cuda") -> VerifyBatch:
+    """Host-side scheduler bookkeeping for one verifier step: token rows,
+    positions and cache slots from the block tables (numpy in, device out)."""
+    t0 = np.asarray(t0, dtype=np.int32)
+    cand = np.asarray(cand, dtype=np.int32)
+    ctx = np.asarray(ctx, dtype=np.int32)
+    bt = np.asarray(block_table, dtype=np.int32)
+    R, K = cand.shape
+    toks = np.concatenate([t0[:, None], cand[:, :K - 1]], axis=1).reshape(-1)
+    pos = (ctx[:, None] + np.arange(K, dtype=np.int32)[None, :]).reshape(-1)
+    rows = np.repeat(np.arange(R), K)
+    slots = bt[rows, pos // 16].astype(np.int64) * 16 + pos % 16
+    if (bt[rows, pos // 16] < 0).any():
+        raise ValueError("block table does not cover positions L_r .. L_r+K-1")
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    nz = noise if isinstance(noise, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(noise, dtype=np.float32))
+    return VerifyBatch(
+        K=K, tokens=dev(toks), pos=dev(pos), ctx=dev(ctx), block_table=dev(bt), slots=dev(slots), cand=dev(cand),
+        noise=nz.reshape(R * K, -1).to(device), target=torch.empty((R, K), dtype=torch.int32, device=device),
+        accept_len=torch.empty(R, dtype=torch.int32, device=device),
+        next_token=torch.empty(R, dtype=torch.int32, device=device))
+
+
+def self_consistent_candidates(model, t0, ctx, block_table, noise, caches, K, first=None, **kw):
+    """Candidates that equal the verifier's own targets at every position.
+
+    Target j depends on the inputs at positions <= j, i.e. on candidates
+    0 .. j-1, so feeding the targets back as candidates fixes at least one
+    more position per pass; K passes reach the fixed point.  Used to plant a
+    first divergence at a chosen position (accept_len must then equal it).
+    """
+    R = len(t0)
+    cand = np.zeros((R, K), np.int32) if first is None else np.asarray(first, np.int32)
+    for _ in range(K):
+        b = make_batch(t0, cand, ctx, block_table, noise)
+        _, tgt, _, _ = model.verify(b, caches, **kw)
+        new = tgt.cpu().numpy()
+        if np.array_equal(new, cand):
+            break
+        cand = new
+    return cand
+
+
+def rollback(ctx, accept_len, next_token, cand):
+    """Host rule after a verification: keep the accepted prefix, take the
+    verifier's token at the first divergence, and continue from there.
+    Returns (new ctx, committed tokens per request, new reference token)."""
+    ctx = np.asarray(ctx)
+    a = np.asarray(accept_len)
+    nx = np.asarray(next_token)
+    cand = np.asarray(cand)
+    K = cand.shape[1]
+    out_ctx = ctx + np.minimum(a + 1, K)
+    committed, t0 = [], []
+    for r in range(len(ctx)):
+        toks = list(cand[r, :a[r]]) + ([int(nx[r])] if a[r] < K else [])
+        committed.append([int(t) for t in toks])
+        t0.append(int(toks[-1]))
+    return out_ctx.astype(np.int32), committed, np.asarray(t0, dtype=np.int32)

@@ -27,6 +27,7 @@ from .ops import (  # noqa: F401
     as_f64,
     attention,
     decoder_forward,
+    gumbel_sample,
     gumbel_verify,
     kv_overwrite,
     linear,

@@ -244,7 +244,7 @@ def decoder_forward(w, tokens, ctx, k_caches, v_caches, block_table, block=16):
     return linear(rmsnorm(x, w["final_norm"], sh.eps), w["lm_head"])
 
 
-def _sample(logits64, noise32):
+def gumbel_sample(logits64, noise32):
     """Gumbel-max sample of one row: the logits are rounded once to fp32 (the
     verify rule is defined on fp32 logits) before s = fl32(logit + g)."""
     t, _, _ = gumbel_verify(np.asarray(logits64, dtype=np.float32)[None, None, :],
@@ -266,7 +266,7 @@ def sequential_decode(w, t0, ctx, k_caches, v_caches, block_table, steps, noise_
     for s in range(steps):
         logits = decoder_forward(w, cur[:, None], c, k_caches, v_caches, block_table, block)
         for r in range(R):
-            out[r, s] = _sample(logits[r], noise_fn(r, int(c[r]) + 1))
+            out[r, s] = gumbel_sample(logits[r], noise_fn(r, int(c[r]) + 1))
         cur = out[:, s].astype(np.int64)
         c = c + 1
     return out

@@ -1,0 +1,98 @@
+"""The C-ABI library loads and exports every function include/biverify.h
+declares; host-side argument checks reject bad calls without launching (CPU
+only: no compute call reaches the GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "biverify.h")
+LIB = os.path.join(ROOT, "invariant_verify_verifier_amd", "libbiverify.so")
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    names = re.findall(r"^(?:biv_status|int|size_t|const char\*)\s+(\w+)\s*\(", txt, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_five_hot_path_calls():
+    names = declared_functions()
+    for n in ["rmsnorm_bi", "gemm_bi", "attn_decode_bi", "gumbel_verify", "kv_overwrite"]:
+        assert n in names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail(f"{LIB} not built (run __graft_entry__.build())")
+    return ctypes.CDLL(LIB)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_covers_every_declared_symbol():
+    import invariant_verify_verifier_amd as m
+
+    assert sorted(m.exported_symbols()) == declared_functions()
+
+
+def test_host_side_argument_errors(lib):
+    """Bad sizes, dtypes and NULL pointers return BIV_EINVAL before any launch."""
+    lib.biv_last_error.restype = ctypes.c_char_p
+    vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    lib.gemm_bi.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, i32, vp]
+    assert lib.gemm_bi(None, None, None, 4, 8, 8, 1, 1, 0, None) == 1  # NULL pointers
+    assert b"NULL" in lib.biv_last_error()
+    assert lib.gemm_bi(None, None, None, 4, 8, 8, 7, 1, 0, None) == 1  # bad dtype
+    assert lib.gemm_bi(None, None, None, 0, 8, 8, 1, 1, 0, None) == 0  # M = 0: nothing to do
+    lib.rmsnorm_bi.argtypes = [vp, i32, vp, vp, i32, i64, i64, f32, vp]
+    assert lib.rmsnorm_bi(None, 0, None, None, 0, 3, 0, 1e-6, None) == 1
+    lib.gumbel_verify.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, vp, vp]
+    assert lib.gumbel_verify(None, None, None, 2, 0, 8, None, None, None, None) == 1  # K = 0
+    assert lib.gumbel_verify(None, None, None, 0, 4, 8, None, None, None, None) == 0  # R = 0
+    lib.kv_overwrite.argtypes = [vp, vp, i64, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    assert lib.kv_overwrite(None, None, 4, None, None, None, 1, 8, 128, 10, 1, None) == 1  # stride < Hkv*D
+    lib.attn_decode_bi.argtypes = [vp, i64, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp,
+                                   ctypes.c_size_t, vp]
+    # Hq not a multiple of Hkv
+    assert lib.attn_decode_bi(None, 4096, None, None, None, None, None, 1, 1, 30, 8, 128, 4, 4, 0.1, 1, None, 0,
+                              None) == 1
+    # bf16 path with too many rows per KV head (q_len * G > 32) is unsupported, not invalid
+    buf = ctypes.create_string_buffer(64)
+    p = ctypes.cast(buf, vp)
+    st = lib.attn_decode_bi(p, 4096, p, p, p, p, p, 1, 16, 32, 8, 128, 4, 4, 0.1, 1, p, 64, None)
+    assert st == 2
+
+
+def test_workspace_sizes(lib):
+    lib.biv_attn_workspace_bytes.restype = ctypes.c_size_t
+    lib.biv_attn_workspace_bytes.argtypes = [ctypes.c_int] * 4
+    n = lib.biv_attn_workspace_bytes(64, 8, 513, 1024)
+    nseg = -(-513 * 16 // 1024)
+    assert n == 2048 + 64 * 8 * nseg * (4096 + 128) * 4
+    lib.biv_splitk_auto_splits.restype = ctypes.c_int
+    lib.biv_splitk_auto_splits.argtypes = [ctypes.c_int64] * 3
+    assert lib.biv_splitk_auto_splits(1, 14336, 4096) > 1  # small M -> split K
+    assert lib.biv_splitk_auto_splits(512, 14336, 4096) == 2
+
+
+def test_rope_table_host_values(lib):
+    """The library's host RoPE table: pos 3, pair 0 turns by 3 rad; pair i by
+    3 * theta^(-2i/D)."""
+    import math
+
+    lib.biv_rope_table.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_double]
+    D, P = 8, 5
+    buf = (ctypes.c_float * (P * D))()
+    assert lib.biv_rope_table(ctypes.cast(buf, ctypes.c_void_p), P, D, 100.0) == 0
+    for i in range(D // 2):
+        a = 3 * 100.0 ** (-2 * i / D)
+        assert abs(buf[(3 * D // 2 + i) * 2] - math.cos(a)) < 1e-7
+        assert abs(buf[(3 * D // 2 + i) * 2 + 1] - math.sin(a)) < 1e-7

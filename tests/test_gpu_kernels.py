@@ -1,0 +1,510 @@
+"""GPU parity of each kernel against the CPU oracle, and batch invariance of
+the "_bi" kernels checked bitwise on the GPU itself.
+
+Parity: bit-exact for gumbel_verify and kv_overwrite (integer/byte work and an
+argmax taken in the same fp32 precision on both sides); tolerances from
+tests/tolerances.py for floating point.  Invariance (LLM-42 post, paragraph 1:
+the same result whatever the batch size): a row's output bits must not change
+with M, with its position in the batch or with the rows next to it.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from gpu_util import DEV, announce, bits, dev_bf16, dev_f32, dev_i32, dev_i64, f64, sync
+from tolerances import check_bf16, check_f32
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def biv():
+    import invariant_verify_verifier_amd as m
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return m
+
+
+# =====================================================================
+# gumbel_verify
+# =====================================================================
+
+
+def _plant_ties(logits, noise, frac_near, frac_exact, seed):
+    """Plant near-ties (0 < top-2 gap of s < 1e-3) and exact fp32 ties in the
+    perturbed scores s = fl32(l + g) of some rows, on either side of the max."""
+    g = wl.rng(seed)
+    R, K, V = logits.shape
+    s = oracle.perturbed_scores(logits, noise)
+    rows = [(r, j) for r in range(R) for j in range(K)]
+    n_near = int(round(frac_near * len(rows)))
+    n_exact = int(round(frac_exact * len(rows)))
+    pick = g.permutation(len(rows))
+    planted_exact = 0
+    for k, idx in enumerate(pick[:n_near]):
+        r, j = rows[idx]
+        t = int(np.argmax(s[r, j]))
+        u = int(g.integers(0, V - 1))
+        u = u + (u >= t)
+        want = np.float32(s[r, j, t])
+        if k < n_exact:
+            lu = np.float32(want - noise[r, j, u])
+            for _ in range(64):
+                got = np.float32(lu + noise[r, j, u])
+                if got == want:
+                    break
+                lu = np.nextafter(lu, np.float32(np.inf) if got < want else np.float32(-np.inf), dtype=np.float32)
+            if np.float32(lu + noise[r, j, u]) == want:
+                logits[r, j, u] = lu
+                planted_exact += 1
+        else:
+            delta = np.float32(g.uniform(1e-5, 1e-3))
+            logits[r, j, u] = np.float32(want - delta - noise[r, j, u])
+    return planted_exact
+
+
+def _verify_case(biv, R, K, V, seed, near=0.05, exact=0.01, offset=0):
+    logits = wl.normal_f32(seed, (R, K, V), std=3.0)
+    noise = wl.gumbel_noise(seed + 3, np.repeat(np.arange(R), K), np.tile(np.arange(K) + 5000, R), V).reshape(R, K, V)
+    n_exact = _plant_ties(logits, noise, near, exact, seed + 1)
+    t0, _, _ = oracle.gumbel_verify(logits, noise, np.zeros((R, K), np.int32))
+    d = wl.rng(seed + 2).integers(0, K + 1, size=R)
+    cand = wl.plant_divergence(t0, d, V, seed + 2)
+    t_ref, a_ref, n_ref = oracle.gumbel_verify(logits, noise, cand)
+    assert np.array_equal(a_ref, d)
+    if offset:  # misaligned rows: exercise the scalar path
+        lg = torch.zeros(R * K * V + offset, dtype=torch.float32, device=DEV)
+        nz = torch.zeros_like(lg)
+        lg[offset:] = dev_f32(logits.reshape(-1))
+        nz[offset:] = dev_f32(noise.reshape(-1))
+        lg, nz = lg[offset:].view(R * K, V), nz[offset:].view(R * K, V)
+    else:
+        lg, nz = dev_f32(logits.reshape(R * K, V)), dev_f32(noise.reshape(R * K, V))
+    c = dev_i32(cand)
+    tgt = torch.full((R, K), -7, dtype=torch.int32, device=DEV)
+    acc = torch.full((R,), -7, dtype=torch.int32, device=DEV)
+    nxt = torch.full((R,), -7, dtype=torch.int32, device=DEV)
+    announce("gumbel_verify", R, K, V, seed, offset)
+    biv.gumbel_verify(lg, nz, c, tgt, acc, nxt)
+    sync()
+    assert np.array_equal(tgt.cpu().numpy(), t_ref)
+    assert np.array_equal(acc.cpu().numpy(), a_ref)
+    assert np.array_equal(nxt.cpu().numpy(), n_ref)
+    return n_exact
+
+
+def test_gumbel_verify_full_size_bitwise(biv):
+    """Full-size coupled verify: fp32 logits [64, 8, 128256] ~ N(0, 9), near-ties
+    in 5% of rows (1% exact), first divergence d ~ U{0..8}."""
+    n_exact = _verify_case(biv, 64, 8, 128256, seed=30)
+    assert n_exact >= 3
+
+
+@pytest.mark.parametrize("R,K,V,offset", [(3, 4, 4099, 0), (2, 3, 1000, 1), (5, 1, 257, 0), (1, 8, 2, 0),
+                                          (16, 4, 4096, 0)])
+def test_gumbel_verify_edge_shapes_bitwise(biv, R, K, V, offset):
+    _verify_case(biv, R, K, V, seed=40 + V % 7, near=0.5, exact=0.25, offset=offset)
+
+
+def test_gumbel_verify_nan_inf_rows(biv):
+    V = 1000
+    l = wl.normal_f32(5, (2, 3, V))
+    g = np.zeros((2, 3, V), np.float32)
+    l[0, 0, :] = np.nan
+    l[0, 1, ::2] = np.nan
+    l[0, 2, :] = -np.inf
+    l[1, 0, 17] = np.inf
+    l[1, 1, 5] = np.float32(-0.0)
+    l[1, 1, :] = np.float32(-1.0)
+    l[1, 1, 5] = np.float32(-0.0)
+    l[1, 1, 3] = np.float32(0.0)
+    cand = np.zeros((2, 3), np.int32)
+    t_ref, a_ref, n_ref = oracle.gumbel_verify(l, g, cand)
+    tgt = torch.empty((2, 3), dtype=torch.int32, device=DEV)
+    acc = torch.empty(2, dtype=torch.int32, device=DEV)
+    nxt = torch.empty(2, dtype=torch.int32, device=DEV)
+    announce("gumbel_verify nan/inf")
+    biv.gumbel_verify(dev_f32(l.reshape(6, V)), dev_f32(g.reshape(6, V)), dev_i32(cand), tgt, acc, nxt)
+    sync()
+    assert np.array_equal(tgt.cpu().numpy(), t_ref)
+    assert t_ref[0, 0] == 0 and t_ref[1, 1] == 3 and t_ref[1, 0] == 17
+    assert np.array_equal(acc.cpu().numpy(), a_ref) and np.array_equal(nxt.cpu().numpy(), n_ref)
+
+
+# =====================================================================
+# kv_overwrite
+# =====================================================================
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_kv_overwrite_bitwise(biv, dtype):
+    """Only the named slots change, to the exact source bits; slots outside
+    the cache are skipped; the source may be a strided slice of a fused row."""
+    nb, Hkv, D, T = 37, 8, 128, 50
+    g = wl.rng(3)
+    slots = g.permutation(nb * 16)[:T].astype(np.int64)
+    slots[7] = -1
+    slots[13] = nb * 16 + 5
+    width = 3 * Hkv * D
+    if dtype == "bf16":
+        src_np = wl.normal_bf16(4, (T, width))
+        kc_np = wl.normal_bf16(5, (nb, Hkv, 16, D))
+        vc_np = wl.normal_bf16(6, (nb, Hkv, 16, D))
+        src, kc, vc = dev_bf16(src_np), dev_bf16(kc_np), dev_bf16(vc_np)
+    else:
+        src_np = wl.normal_f32(4, (T, width))
+        kc_np = wl.normal_f32(5, (nb, Hkv, 16, D))
+        vc_np = wl.normal_f32(6, (nb, Hkv, 16, D))
+        src, kc, vc = dev_f32(src_np), dev_f32(kc_np), dev_f32(vc_np)
+    kref, vref = kc_np.copy(), vc_np.copy()
+    kn = src_np[:, Hkv * D:2 * Hkv * D].reshape(T, Hkv, D)
+    vn = src_np[:, 2 * Hkv * D:].reshape(T, Hkv, D)
+    ok = (slots >= 0) & (slots < nb * 16)
+    oracle.kv_overwrite(kref, vref, kn[ok], vn[ok], slots[ok])
+    announce("kv_overwrite", dtype)
+    biv.kv_overwrite(src[:, Hkv * D:2 * Hkv * D], src[:, 2 * Hkv * D:], dev_i64(slots), kc, vc)
+    sync()
+    assert np.array_equal(bits(kc), kref.view(bits(kc).dtype))
+    assert np.array_equal(bits(vc), vref.view(bits(vc).dtype))
+
+
+# =====================================================================
+# rmsnorm_bi
+# =====================================================================
+
+M_SWEEP = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512]
+
+
+def test_rmsnorm_bf16_parity_and_invariance(biv):
+    """bf16 activations [M, 4096] ~ N(0,1), gamma ~ N(1, 0.1), eps 1e-6."""
+    H = 4096
+    x_np = wl.normal_bf16(10, (512, H))
+    g_np = wl.normal_bf16(11, (H,), std=0.1, mean=1.0)
+    x, gam = dev_bf16(x_np), dev_bf16(g_np)
+    announce("rmsnorm bf16 M=512")
+    y = torch.empty_like(x)
+    biv.rmsnorm_bi(x, gam, y, 1e-6)
+    sync()
+    ref = oracle.rmsnorm(oracle.as_f64(x_np, "bf16"), oracle.as_f64(g_np, "bf16"), 1e-6)
+    check_bf16(f64(y), ref, "rmsnorm bf16")
+    full = bits(y)
+    for M in M_SWEEP:
+        yM = torch.empty((M, H), dtype=torch.bfloat16, device=DEV)
+        biv.rmsnorm_bi(x[:M].contiguous(), gam, yM, 1e-6)
+        sync()
+        assert np.array_equal(bits(yM), full[:M]), f"rows changed at M={M}"
+    perm = wl.rng(1).permutation(512)
+    yp = torch.empty_like(x)
+    biv.rmsnorm_bi(x[torch.from_numpy(perm).to(DEV)].contiguous(), gam, yp, 1e-6)
+    sync()
+    assert np.array_equal(bits(yp), full[perm])
+
+
+def test_rmsnorm_f32_and_mixed(biv):
+    H = 256
+    x_np = wl.normal_f32(12, (37, H), std=2.0)
+    g_np = wl.normal_f32(13, (H,), std=0.1, mean=1.0)
+    ref = oracle.rmsnorm(x_np.astype(np.float64), g_np.astype(np.float64), 1e-6)
+    y = torch.empty((37, H), dtype=torch.float32, device=DEV)
+    announce("rmsnorm f32")
+    biv.rmsnorm_bi(dev_f32(x_np), dev_f32(g_np), y, 1e-6)
+    sync()
+    check_f32(f64(y), ref, what="rmsnorm f32")
+    # fp32 residual stream -> bf16 normalised activations
+    gb = wl.bf16_bits(g_np)
+    ref2 = oracle.rmsnorm(x_np.astype(np.float64), oracle.as_f64(gb, "bf16"), 1e-6)
+    y2 = torch.empty((37, H), dtype=torch.bfloat16, device=DEV)
+    biv.rmsnorm_bi(dev_f32(x_np), dev_bf16(gb), y2, 1e-6)
+    sync()
+    check_bf16(f64(y2), ref2, "rmsnorm f32->bf16")
+
+
+# =====================================================================
+# gemm_bi
+# =====================================================================
+
+
+def test_gemm_bf16_exact_integer_operands(biv):
+    """Integer operands in {-2..2}: every partial sum is an exact fp32 integer
+    (|sum| <= 4*4096 < 2^24), so any correct reduction equals the exact
+    product -- the GPU must match the oracle bit for bit (fp32 output)."""
+    M, N, K = 100, 300, 4096
+    g = wl.rng(7)
+    a = g.integers(-2, 3, size=(M, K)).astype(np.float32)
+    b = g.integers(-2, 3, size=(N, K)).astype(np.float32)
+    c = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    announce("gemm bf16 exact ints")
+    biv.gemm_bi(dev_bf16(wl.bf16_bits(a)), dev_bf16(wl.bf16_bits(b)), c)
+    sync()
+    assert np.array_equal(c.cpu().numpy().astype(np.float64), oracle.linear(a, b))
+
+
+def _cfg1_weight(N=14336, K=4096):
+    """The microbench weight is [4096, 14336] ~ N(0, 0.02); the GEMM takes it in
+    linear-layer layout [N, K] (a one-time transpose, off the timed path)."""
+    w = wl.normal_bf16(12, (K, N), std=0.02)
+    return np.ascontiguousarray(w.T)
+
+
+def test_gemm_bf16_cfg1_parity_and_invariance(biv):
+    """[M, 4096] x [4096, 14336], bf16 in, fp32 accumulate; every row's bits
+    identical for M = 1, 2, 4, ..., 512 and under a row shuffle."""
+    K, N = 4096, 14336
+    a_np = wl.normal_bf16(10, (512, K))
+    w_np = _cfg1_weight(N, K)
+    a, w = dev_bf16(a_np), dev_bf16(w_np)
+    announce("gemm bf16 cfg1 M=512")
+    c = torch.empty((512, N), dtype=torch.bfloat16, device=DEV)
+    biv.gemm_bi(a, w, c)
+    cf = torch.empty((512, N), dtype=torch.float32, device=DEV)
+    biv.gemm_bi(a, w, cf)
+    sync()
+    ref = oracle.linear(oracle.as_f64(a_np, "bf16"), oracle.as_f64(w_np, "bf16"))
+    check_bf16(f64(c), ref, "gemm bf16 out")
+    check_f32(f64(cf), ref, axis=1, what="gemm fp32 out")
+    full = bits(c)
+    for M in M_SWEEP:
+        cM = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+        biv.gemm_bi(a[:M].contiguous(), w, cM)
+        sync()
+        assert np.array_equal(bits(cM), full[:M]), f"rows changed at M={M}"
+    perm = wl.rng(2).permutation(512)
+    cp = torch.empty_like(c)
+    biv.gemm_bi(a[torch.from_numpy(perm).to(DEV)].contiguous(), w, cp)
+    sync()
+    assert np.array_equal(bits(cp), full[perm])
+
+
+@pytest.mark.parametrize("M,N,K", [(77, 200, 264), (1, 130, 8), (129, 257, 1000), (300, 128, 4096)])
+def test_gemm_bf16_ragged_shapes(biv, M, N, K):
+    a_np = wl.normal_bf16(20 + M, (M, K))
+    w_np = wl.normal_bf16(21 + N, (N, K), std=0.05)
+    c = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    announce("gemm bf16 ragged", M, N, K)
+    biv.gemm_bi(dev_bf16(a_np), dev_bf16(w_np), c)
+    sync()
+    ref = oracle.linear(oracle.as_f64(a_np, "bf16"), oracle.as_f64(w_np, "bf16"))
+    check_f32(f64(c), ref, axis=1, what="ragged gemm")
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_gemm_accumulate_epilogue(biv, out):
+    M, N, K = 64, 256, 512
+    a_np = wl.normal_bf16(30, (M, K))
+    w_np = wl.normal_bf16(31, (N, K), std=0.05)
+    r_np = wl.normal_f32(32, (M, N))
+    if out == "f32":
+        c = dev_f32(r_np)
+        r64 = r_np.astype(np.float64)
+    else:
+        rb = wl.bf16_bits(r_np)
+        c = dev_bf16(rb)
+        r64 = oracle.as_f64(rb, "bf16")
+    announce("gemm accumulate", out)
+    biv.gemm_bi(dev_bf16(a_np), dev_bf16(w_np), c, accumulate=True)
+    sync()
+    ref = r64 + oracle.linear(oracle.as_f64(a_np, "bf16"), oracle.as_f64(w_np, "bf16"))
+    if out == "f32":
+        check_f32(f64(c), ref, axis=1, what="accumulate f32")
+    else:
+        check_bf16(f64(c), ref, "accumulate bf16")
+
+
+def test_gemm_f32_parity_and_invariance(biv):
+    M, N, K = 16, 1024, 256
+    a_np = wl.normal_f32(40, (M, K))
+    w_np = wl.normal_f32(41, (N, K), std=0.02)
+    a, w = dev_f32(a_np), dev_f32(w_np)
+    c = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    announce("gemm f32")
+    biv.gemm_bi(a, w, c)
+    sync()
+    check_f32(f64(c), oracle.linear(a_np, w_np), axis=1, what="gemm f32")
+    full = bits(c)
+    for m in range(1, M + 1):
+        cm = torch.empty((m, N), dtype=torch.float32, device=DEV)
+        biv.gemm_bi(a[:m].contiguous(), w, cm)
+        sync()
+        assert np.array_equal(bits(cm), full[:m])
+    # ragged K and N on the fp32 path
+    a2 = wl.normal_f32(42, (5, 37))
+    w2 = wl.normal_f32(43, (70, 37))
+    c2 = torch.empty((5, 70), dtype=torch.float32, device=DEV)
+    biv.gemm_bi(dev_f32(a2), dev_f32(w2), c2)
+    sync()
+    check_f32(f64(c2), oracle.linear(a2, w2), axis=1, what="gemm f32 ragged")
+
+
+# =====================================================================
+# attn_decode_bi
+# =====================================================================
+
+
+def _attn_inputs(R, q_len, Hq, Hkv, D, ctx, seed, dtype="bf16", spare=3):
+    lay = wl.paged_layout(ctx, q_len, seed=seed, spare_blocks=spare)
+    mk = wl.normal_bf16 if dtype == "bf16" else wl.normal_f32
+    kc = mk(seed + 1, (lay.num_blocks, Hkv, 16, D))
+    vc = mk(seed + 2, (lay.num_blocks, Hkv, 16, D))
+    q = mk(seed + 3, (R * q_len, Hq, D))
+    return lay, kc, vc, q
+
+
+def _run_attn(biv, lay, kc, vc, q, q_len, dtype="bf16", fn=None, **kw):
+    dev = dev_bf16 if dtype == "bf16" else dev_f32
+    T, Hq, D = q.shape
+    out = torch.full((T, Hq, D), float("nan"), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32,
+                     device=DEV)
+    kcd, vcd = dev(kc), dev(vc)
+    bt, cx = dev_i32(lay.block_table), dev_i32(lay.ctx)
+    ws = None
+    if dtype == "bf16":
+        nbytes = biv.attn_workspace_bytes(len(lay.ctx), kc.shape[1], lay.max_blocks, kw.pop("seg", 1024))
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    (fn or biv.attn_decode_bi)(dev(q), kcd, vcd, bt, cx, out, q_len, 1.0 / math.sqrt(D), ws, **kw)
+    sync()
+    return out
+
+
+def _attn_ref(lay, kc, vc, q, q_len, dtype="bf16"):
+    return oracle.attention(oracle.as_f64(q, dtype), oracle.as_f64(kc, dtype), oracle.as_f64(vc, dtype),
+                            lay.block_table, lay.ctx, q_len, 1.0 / math.sqrt(q.shape[-1]))
+
+
+@pytest.mark.parametrize("q_len", [1, 8])
+def test_attention_bf16_parity(biv, q_len):
+    """32 q heads / 8 KV heads x 128, paged KV (16-token pages, permuted),
+    contexts spanning several 256-token chunks and 1024-token segments plus
+    ragged tails and exact boundaries."""
+    ctx = [0, 255 - q_len + 1, 256, 1023, 1024, 1025, 2500, 5000]
+    R = len(ctx)
+    lay, kc, vc, q = _attn_inputs(R, q_len, 32, 8, 128, ctx, seed=50 + q_len)
+    announce("attention bf16 parity q_len", q_len)
+    out = _run_attn(biv, lay, kc, vc, q, q_len)
+    ref = _attn_ref(lay, kc, vc, q, q_len)
+    check_bf16(f64(out), ref, f"attention bf16 q_len={q_len}")
+    # a single visible key returns its value exactly
+    v0 = oracle.as_f64(vc, "bf16")[lay.block_table[0, 0], :, 0, :]  # [Hkv, D]
+    got = f64(out)[0]  # request 0, row 0
+    for h in range(32):
+        assert np.array_equal(got[h], v0[h // 4])
+
+
+def test_attention_bf16_batch_invariance(biv):
+    """Request 0's outputs are bit-identical alone, at another batch slot,
+    with other requests next to it, and with its pages elsewhere in memory."""
+    q_len, Hq, Hkv, D = 8, 32, 8, 128
+    base_ctx = 3000
+    lay, kc, vc, q = _attn_inputs(1, q_len, Hq, Hkv, D, [base_ctx], seed=60)
+    announce("attention invariance alone")
+    alone = bits(_run_attn(biv, lay, kc, vc, q, q_len))
+    g = wl.rng(61)
+    for trial in range(3):
+        R = int(g.integers(2, 12))
+        slot = int(g.integers(0, R))
+        ctx = list(g.integers(500, 9000, size=R))
+        ctx[slot] = base_ctx
+        lay2 = wl.paged_layout(ctx, q_len, seed=62 + trial, spare_blocks=int(g.integers(0, 9)))
+        kc2 = wl.normal_bf16(63 + trial, (lay2.num_blocks, Hkv, 16, D))
+        vc2 = wl.normal_bf16(64 + trial, (lay2.num_blocks, Hkv, 16, D))
+        q2 = wl.normal_bf16(65 + trial, (R * q_len, Hq, D))
+        # copy request 0's pages and queries into the new layout at `slot`
+        for b in range(lay.max_blocks):
+            src, dst = lay.block_table[0, b], lay2.block_table[slot, b]
+            if src >= 0:
+                kc2[dst] = kc[src]
+                vc2[dst] = vc[src]
+        q2[slot * q_len:(slot + 1) * q_len] = q
+        announce("attention invariance trial", trial, R, slot)
+        out2 = bits(_run_attn(biv, lay2, kc2, vc2, q2, q_len))
+        assert np.array_equal(out2[slot * q_len:(slot + 1) * q_len], alone), f"trial {trial}"
+
+
+def test_attention_bf16_verify_rows_equal_single_decodes(biv):
+    """Row j of a K=8 verify block equals, bit for bit, the same query decoded
+    alone (K=1) at context L+j: extra masked keys and chunks fold as no-ops."""
+    q_len, Hq, Hkv, D, L = 8, 32, 8, 128, 1530  # crosses a chunk and a segment boundary
+    lay, kc, vc, q = _attn_inputs(1, q_len, Hq, Hkv, D, [L], seed=70)
+    announce("attention verify vs decode")
+    block = bits(_run_attn(biv, lay, kc, vc, q, q_len))
+    for j in range(q_len):
+        lay1 = wl.PagedLayout(ctx=np.array([L + j], np.int32), q_len=1, block_table=lay.block_table,
+                              num_blocks=lay.num_blocks, max_blocks=lay.max_blocks)
+        one = bits(_run_attn(biv, lay1, kc, vc, q[j:j + 1], 1))
+        assert np.array_equal(one[0], block[j]), f"row {j}"
+
+
+def test_attention_f32_parity(biv):
+    """fp32 path (tiny model: 4 heads x 64, no grouping), decode, verify and
+    prefill-shaped calls."""
+    for q_len, ctx in [(1, [0, 5, 300]), (4, [128, 17, 600]), (128, [0])]:
+        R = len(ctx)
+        lay, kc, vc, q = _attn_inputs(R, q_len, 4, 4, 64, ctx, seed=80 + q_len, dtype="f32")
+        announce("attention f32", q_len, ctx)
+        out = _run_attn(biv, lay, kc, vc, q, q_len, dtype="f32")
+        check_f32(f64(out), _attn_ref(lay, kc, vc, q, q_len, "f32"), what=f"attention f32 q_len={q_len}")
+
+
+def test_attention_adaptive_matches_oracle(biv):
+    q_len = 1
+    ctx = [600, 4000, 9000, 12000]
+    lay, kc, vc, q = _attn_inputs(len(ctx), q_len, 32, 8, 128, ctx, seed=90)
+    split = biv.attn_adaptive_split(len(ctx), 8, lay.max_blocks)
+    announce("attention adaptive split", split)
+    out = _run_attn(biv, lay, kc, vc, q, q_len, fn=biv.attn_decode_adaptive, seg=split)
+    check_bf16(f64(out), _attn_ref(lay, kc, vc, q, q_len), "attention adaptive")
+
+
+# =====================================================================
+# split-K, RoPE, SwiGLU, embedding
+# =====================================================================
+
+
+@pytest.mark.parametrize("M", [1, 16, 512])
+def test_gemm_splitk_matches_oracle(biv, M):
+    K, N = 4096, 2048
+    a_np = wl.normal_bf16(100 + M, (M, K))
+    w_np = wl.normal_bf16(101, (N, K), std=0.02)
+    sp = biv.splitk_auto_splits(M, N, K)
+    ws = torch.empty(biv.splitk_workspace_bytes(M, N, sp) // 4 + 1, dtype=torch.float32, device=DEV)
+    c = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    announce("gemm splitk", M, sp)
+    biv.gemm_splitk(dev_bf16(a_np), dev_bf16(w_np), c, 0, ws)
+    sync()
+    ref = oracle.linear(oracle.as_f64(a_np, "bf16"), oracle.as_f64(w_np, "bf16"))
+    check_f32(f64(c), ref, axis=1, what="splitk")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rope_swiglu_embed(biv, dtype):
+    dev = dev_bf16 if dtype == "bf16" else dev_f32
+    mk = wl.normal_bf16 if dtype == "bf16" else wl.normal_f32
+    chk = (lambda g, r, w: check_bf16(g, r, w)) if dtype == "bf16" else (lambda g, r, w: check_f32(g, r, what=w))
+    T, H, D = 9, 6, 128
+    x_np = mk(110, (T, (H + 2) * D))
+    pos = np.array([0, 1, 7, 100, 2047, 5000, 8191, 30000, 65535], np.int32)
+    x = dev(x_np)
+    table = biv.rope_table(65536, D, 500000.0).to(DEV)
+    announce("rope", dtype)
+    biv.rope_apply(x, dev_i32(pos), table, H, D)
+    sync()
+    ref = oracle.as_f64(x_np, dtype).copy()
+    ref[:, :H * D] = oracle.rope(ref[:, :H * D].reshape(T, H, D), pos, 500000.0).reshape(T, H * D)
+    chk(f64(x), ref, "rope")
+    gu_np = mk(111, (33, 2 * 300))
+    out = torch.empty((33, 300), dtype=x.dtype, device=DEV)
+    biv.swiglu(dev(gu_np), out)
+    sync()
+    gu = oracle.as_f64(gu_np, dtype)
+    chk(f64(out), oracle.silu(gu[:, :300]) * gu[:, 300:], "swiglu")
+    tab_np = mk(112, (50, 64))
+    ids = np.array([3, 49, 0, 7, -1, 50], np.int32)
+    emb = torch.empty((6, 64), dtype=torch.float32, device=DEV)
+    biv.embed_rows(dev_i32(ids), dev(tab_np), emb)
+    sync()
+    ref = np.zeros((6, 64))
+    ref[:4] = oracle.as_f64(tab_np, dtype)[ids[:4]]
+    assert np.array_equal(f64(emb), ref)

@@ -292,3 +292,63 @@ def ceil_div(a: int, b: int) -> int:
 
 
 __all__ = [name for name in dir() if not name.startswith("_") and name not in ("annotations", "math")]
+
+
+# ---------------------------------------------------------------------------
+# Device-side generation for the 8B-shaped decoder (15 GB of weights, tens of
+# GB of KV): seeded torch generators on the GPU, N(0, std^2) drawn in fp32 and
+# rounded once to bf16.  The same tensors, copied to the host, feed the oracle.
+# ---------------------------------------------------------------------------
+
+
+def _torch_normal(shape, seed, stream, std, device, dtype):
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed((int(seed) * 1_000_003 + int(stream)) % (2 ** 63))
+    t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        t.mul_(std)
+    return t.to(dtype)
+
+
+def device_model_weights(shape: ModelShape, seed: int, layers=None, device="cuda", std=0.02):
+    """Random-init decoder weights on the device, bf16, in the fused layout the
+    verifier uses: wqkv = [Wq; Wk; Wv] ([Hq*D + 2*Hkv*D, H]) and w_gu =
+    [W_gate; W_up] ([2F, H]); RMSNorm gains are ones."""
+    import torch
+
+    nl = shape.layers if layers is None else layers
+    H, D, F, V = shape.hidden, shape.head_dim, shape.ffn, shape.vocab
+    bf = torch.bfloat16
+    out = dict(embed=_torch_normal((V, H), seed, 0, std, device, bf),
+               lm_head=_torch_normal((V, H), seed, 1, std, device, bf),
+               final_norm=torch.ones(H, dtype=bf, device=device), layers=[])
+    for li in range(nl):
+        s = 100 + 16 * li
+        out["layers"].append(dict(
+            attn_norm=torch.ones(H, dtype=bf, device=device),
+            wqkv=_torch_normal((shape.qkv_out, H), seed, s + 0, std, device, bf),
+            wo=_torch_normal((H, shape.heads * D), seed, s + 3, std, device, bf),
+            ffn_norm=torch.ones(H, dtype=bf, device=device),
+            w_gu=_torch_normal((2 * F, H), seed, s + 4, std, device, bf),
+            w_down=_torch_normal((H, F), seed, s + 6, std, device, bf),
+        ))
+    return out
+
+
+def device_kv_cache(shape: ModelShape, num_blocks: int, seed: int, layers=None, device="cuda"):
+    """Per-layer paged K/V caches [num_blocks, Hkv, 16, D] bf16 ~ N(0, 1): the
+    context of every request (standing in for a prefill) and independent junk
+    in the fast-path slots the verifier overwrites."""
+    import torch
+
+    nl = shape.layers if layers is None else layers
+    caches = []
+    for li in range(nl):
+        k = _torch_normal((num_blocks, shape.kv_heads, BLOCK, shape.head_dim), seed, 2 * li, 1.0, device,
+                          torch.bfloat16)
+        v = _torch_normal((num_blocks, shape.kv_heads, BLOCK, shape.head_dim), seed, 2 * li + 1, 1.0, device,
+                          torch.bfloat16)
+        caches.append((k, v))
+    return caches
