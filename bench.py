@@ -96,15 +96,14 @@ def setup(torch, n_layers):
 
 def cpu_baseline(torch, env, n_layers):
     """The oracle, untouched, on a bounded sample of the same workload: one
-    decoder layer plus the final norm and lm_head for the first 8 requests
-    (64 of the 512 rows), extrapolated to the full depth as
-    32 * t_layer + t_head per 64 verified tokens."""
+    decoder layer over all 512 rows plus the final norm, lm_head and verify,
+    extrapolated to the full depth as 32 * t_layer + t_head per pass."""
     import oracle
     import workloads as wl
     from threadpoolctl import threadpool_info
 
     sh, dw, lay, ctx = env["sh"], env["dw"], env["lay"], env["ctx"]
-    n = 8
+    n = N_REQ
     H, D, F = sh.hidden, sh.head_dim, sh.ffn
     q, kv = sh.heads * D, sh.kv_heads * D
 
@@ -140,7 +139,7 @@ def cpu_baseline(torch, env, n_layers):
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": round(n * K_CAND / t_pass, 3), "unit": "verified tok/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"1 of {n_layers} layers + lm_head/verify for 8 of 64 requests (64 of 512 rows), fp64; "
+            "sample": f"1 of {n_layers} layers + lm_head/verify over all {n * K_CAND} rows, fp64; "
                       f"t_layer={t_layer:.2f}s t_head={t_head:.2f}s; pass = {n_layers}*t_layer + t_head "
                       f"(extrapolated)"}
 

@@ -133,16 +133,18 @@ biv_status gemm_bi(const void* A, const void* B, void* C, int64_t M, int64_t N, 
  * ascending order.  Every split point is a fixed absolute position, so a
  * row's result depends only on its own request's data and length.
  * Positions >= ctx[r] + q_len read as empty (values zero, keys masked).
+ * Two launches: the chunk/segment pass, then (only when some request spans
+ * more than one segment) the fold of the segment results.
  *
  * Supported: dt BIV_BF16 with D == 128 and q_len * (Hq/Hkv) <= 32 (bf16 MFMA
  * path); dt BIV_F32 with D in {64, 128} (fp32 path, any q_len).  Hq % Hkv == 0,
  * ctx[r] + q_len <= max_blocks * 16.
  *
  * workspace: device memory of at least
- * biv_attn_workspace_bytes(R, Hkv, max_blocks, BIV_ATTN_SEG_TOKENS) bytes (bf16
- * path; may be NULL for the fp32 path).  It must be zero-filled before its first
- * use; every call leaves it ready for the next one.  Calls that share a
- * workspace must be ordered (same stream).
+ * biv_attn_workspace_bytes(R, Hkv, max_blocks, BIV_ATTN_SEG_TOKENS) bytes,
+ * 16-byte aligned (bf16 path; may be NULL for the fp32 path); it holds the
+ * segment results between the two launches and needs no initialisation.
+ * Calls that share a workspace must be ordered (same stream).
  * ------------------------------------------------------------------------ */
 #define BIV_ATTN_CHUNK_TOKENS 256
 #define BIV_ATTN_SEG_TOKENS 1024

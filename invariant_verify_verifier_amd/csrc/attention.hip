@@ -10,16 +10,21 @@
 // bf16 path.  The keys of a request are cut at fixed absolute positions:
 //   sub-tile = 32 keys (one MFMA block), chunk = 256 keys (the KV split),
 //   segment  = seg_tokens keys (1024 for the invariant kernel).
-// One wave per (segment, KV head, request).  For each chunk the wave computes
-// the partial (m, l, o) of its rows: S^T = K Q^T and O^T = V^T P^T on the
-// 32x32x16 bf16 MFMA, softmax statistics in fp32 (log2 domain), rescaled
-// sub-tile by sub-tile in ascending order.  Chunk partials are left-folded in
-// ascending order into the segment result; segment results go to the
-// workspace and the last wave to finish for a (request, KV head) left-folds
-// them in ascending order and writes the output.  The rows of one KV head
-// (q_len positions x G query heads <= 32) share one 32-row MFMA block, so the
-// K/V of a page is read once for all of them (the pages' tile rule: G x (1+D)
-// rows per KV head, here G x K <= 32).
+// One workgroup of four waves per (segment, KV head, request).  Each wave
+// computes the partial (m, l, o) of one chunk for all rows of the KV head:
+// S^T = K Q^T and O^T = V^T P^T on the 32x32x16 bf16 MFMA, softmax statistics
+// in fp32 (log2 domain), rescaled sub-tile by sub-tile in ascending order.
+// The four chunk partials meet in LDS and are left-folded in ascending chunk
+// order into the segment result (each thread folds 16 of the 32 x 128
+// outputs); a segment longer than four chunks repeats this in rounds.
+// Segment results go to the workspace; a second, small kernel left-folds
+// them in ascending order and writes the output (a request with a single
+// segment is written directly).  A kernel boundary, not a device-wide fence,
+// makes the segment results visible: on gfx950 such a fence writes back and
+// invalidates the whole L2 of an XCD, once per workgroup.  The rows of one KV head (q_len positions x G query heads <= 32)
+// share one 32-row MFMA block, so the K/V of a page is read once for all of
+// them (the pages' tile rule: G x (1+D) rows per KV head, here G x K <= 32).
+// K/V pages move from HBM straight into LDS (gfx950 global_load_lds_dwordx4).
 //
 // Every boundary is an absolute position and every fold runs in ascending
 // order, so a row's bits depend only on its own query, its own request's KV
@@ -35,44 +40,61 @@ constexpr int kHD = 128;                 // head dim of the MFMA path
 constexpr int kSub = 32;                 // keys per sub-tile
 constexpr int kChunk = BIV_ATTN_CHUNK_TOKENS;
 constexpr int kSubsPerChunk = kChunk / kSub;
-constexpr int kSubBytes = kSub * kHD * 2;  // 8 KiB
+constexpr int kWaves = 4;                // waves per workgroup = chunks per round
+constexpr int kStage = kSub * kHD * 2 * 2;  // 16 KiB: K and V of one sub-tile
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ int kv_swz(int key, int chunk) { return key * 256 + ((chunk ^ (key & 7)) << 4); }
 
 struct AttnWs {
-  unsigned* counters;  // [R * Hkv]
-  float* part_o;       // [slot][64 values][64 lanes]
-  float* part_ml;      // [slot][64 lanes][2]
+  float* part_o;   // [slot][4096]: element t + 256 k of thread t
+  float* part_ml;  // [slot][64 lanes][2]
 };
 
-__host__ __device__ inline size_t attn_counter_bytes(int R, int Hkv) {
-  return (((size_t)R * Hkv * sizeof(unsigned)) + 255) / 256 * 256;
+// One gfx950 global_load_lds_dwordx4: lane i copies 16 bytes from
+// sbase + voff_i (sbase wave-uniform) to LDS bytes 16i..16i+15 after `dst`
+// (wave-uniform).  Issued as inline asm so that the compiler does not model
+// the LDS write: its own hazard tracking would wait for every outstanding
+// copy before any LDS read, which serialises the K/V pipeline.  Callers order
+// the copies with explicit vmcnt waits; loads the compiler issues itself stay
+// correct, since untracked copies only make its vmcnt waits stricter.  M0
+// (the LDS base of the copy) is not used by anything else in these kernels.
+__device__ __forceinline__ void lds_dma16(const void* sbase, unsigned voff, void* dst) {
+  const unsigned m0v =
+      __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)dst);
+  // readfirstlane yields a signed int: widen each half through uint32_t so
+  // the low half is zero-extended, never sign-extended into the high half
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)sbase);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((unsigned)((uintptr_t)sbase >> 32));
+  const uint64_t sb = (uint64_t)lo | ((uint64_t)hi << 32);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb), "s"(m0v) : "memory");
 }
 
-__device__ __forceinline__ void fold(float& M, float& L, f32x16 (&O)[4], float m, float l, const f32x16 (&o)[4]) {
+// (M, L, O) <- fold((M, L, O), (m, l, o)) for the 16 outputs a thread owns.
+__device__ __forceinline__ void fold16(float& M, float& L, float (&O)[16], float m, float l, const float (&o)[16]) {
   const float mn = fmaxf(M, m);
   if (mn == -INFINITY) return;  // both empty
   const float a = exp2f(M - mn);  // 0 when M == -inf, exactly 1 when M == mn
   const float b = exp2f(m - mn);
   L = __fadd_rn(__fmul_rn(L, a), __fmul_rn(l, b));
 #pragma unroll
-  for (int d = 0; d < 4; ++d)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) O[d][v] = __fadd_rn(__fmul_rn(O[d][v], a), __fmul_rn(o[d][v], b));
+  for (int k = 0; k < 16; ++k) O[k] = __fadd_rn(__fmul_rn(O[k], a), __fmul_rn(o[k], b));
   M = mn;
 }
 
-__global__ __launch_bounds__(64) void attn_bf16_kernel(const uint16_t* __restrict__ q, int64_t q_stride,
-                                                       const uint16_t* __restrict__ k_cache,
-                                                       const uint16_t* __restrict__ v_cache,
-                                                       const int32_t* __restrict__ block_table,
-                                                       const int32_t* __restrict__ ctx, uint16_t* __restrict__ out,
-                                                       int q_len, int Hq, int Hkv, int max_blocks, int num_blocks,
-                                                       float scale_log2, int seg_tokens, int nseg_max, AttnWs ws) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2][2][kSubBytes];  // [buf][K/V]
+__global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
+    const uint16_t* __restrict__ q, int64_t q_stride, const uint16_t* __restrict__ k_cache,
+    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx,
+    uint16_t* __restrict__ out, int q_len, int Hq, int Hkv, int max_blocks, int num_blocks, float scale_log2,
+    int seg_tokens, int nseg_max, AttnWs ws) {
+  // per wave: staging of one sub-tile's K and V (separate arrays, so the
+  // compiler tracks the direct-to-LDS loads of each apart), reused for the
+  // wave's chunk partial
+  __shared__ __attribute__((aligned(16))) unsigned char lds_k[kWaves][kStage / 2];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_v[kWaves][kStage / 2];
+  __shared__ float lds_ml[kWaves][64][2];
   const int seg = blockIdx.x, kvh = blockIdx.y, r = blockIdx.z;
-  const int lane = threadIdx.x, g = lane >> 5, li = lane & 31;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
   const int G = Hq / Hkv, nrows = q_len * G;
   const int L = ctx[r];
   const int n_tok = min(L + q_len, max_blocks * 16);
@@ -89,7 +111,6 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(const uint16_t* __restric
   const int hq = kvh * G + (row_ok ? rho % G : 0);
   const int last_key = row_ok ? L + jq : -1;
   const int64_t qtok = (int64_t)r * q_len + jq;
-  const int64_t orow_off = (qtok * Hq + hq) * kHD;
 
   bf16x8 bq[8];
 #pragma unroll
@@ -102,189 +123,271 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(const uint16_t* __restric
     }
   }
 
-  // staging of a 32-key sub-tile: instruction i covers keys 4i..4i+3,
-  // lane -> key 4i + lane/16, 16-byte chunk lane%16
-  u32x4 rk[8], rv[8];
-  auto load_sub = [&](int sub_base) {
+  unsigned char* Ks = lds_k[wave];
+  unsigned char* Vs = lds_v[wave];
+  const int n_pages = (n_tok + 15) >> 4;
+  // Staging of 32 keys of K (or V) straight from HBM into LDS (gfx950
+  // global_load_lds_dwordx4: no registers, lane i writes bytes 16i..16i+15 of
+  // the instruction's 1 KiB window).  Instruction i covers keys 4i..4i+3, all
+  // in one page; the XOR swizzle of the LDS layout is applied by choosing
+  // which 16-byte chunk of its key each lane fetches.  Keys of a missing page
+  // are fetched from page 0 (in bounds); their values, and those of positions
+  // past the request's last one, are zeroed after landing: a masked key must
+  // contribute exactly nothing, whatever its slot holds.  Each call issues 8
+  // loads, counted by vmcnt in issue order.
+  // byte offset of lane's 16-byte piece within a 4-key, 1 KiB window of a
+  // page: key 4i + lane/16 (row), 16-byte chunk (lane%16) ^ (key%8) (the
+  // swizzle); key%8 = 4(i%2) + lane/16, so two variants cover every i
+  const unsigned voff_even = 256u * (lane >> 4) + 16u * ((lane & 15) ^ (lane >> 4));
+  const unsigned voff_odd = 256u * (lane >> 4) + 16u * ((lane & 15) ^ (4 + (lane >> 4)));
+  auto dma = [&](const uint16_t* cache, unsigned char* dst, int p0, int p1) {
+    const uint16_t* b0 = cache + ((int64_t)(p0 >= 0 ? p0 : 0) * Hkv + kvh) * 16 * kHD;
+    const uint16_t* b1 = cache + ((int64_t)(p1 >= 0 ? p1 : 0) * Hkv + kvh) * 16 * kHD;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const unsigned char* base = reinterpret_cast<const unsigned char*>(i < 4 ? b0 : b1) + 1024 * (i & 3);
+      lds_dma16(base, (i & 1) ? voff_odd : voff_even, dst + 1024 * i);
+    }
+  };
+  auto zero_missing = [&](int sub_base, int p0, int p1) {
+    if (p0 >= 0 && p1 >= 0 && sub_base + kSub <= n_tok) return;  // wave-uniform
+    const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int key = 4 * i + (lane >> 4);
-      const int pos = sub_base + key;
-      const int c = lane & 15;
-      int page = -1;
-      if (pos < n_tok) page = bt[pos >> 4];
-      if (page >= 0 && page < num_blocks) {
-        const int64_t off = (((int64_t)page * Hkv + kvh) * 16 + (pos & 15)) * kHD + 8 * c;
-        rk[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k_cache + off));
-        rv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v_cache + off));
-      } else {
-        rk[i] = u32x4{0u, 0u, 0u, 0u};
-        rv[i] = u32x4{0u, 0u, 0u, 0u};
-      }
+      const bool ok = (i < 4 ? p0 : p1) >= 0 && sub_base + key < n_tok;
+      if (!ok) *reinterpret_cast<u32x4*>(Vs + 1024 * i + 16 * lane) = zero;  // row of key 4i + lane/16
     }
-  };
-  auto store_sub = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int key = 4 * i + (lane >> 4);
-      const int c = lane & 15;
-      *reinterpret_cast<u32x4*>(&lds[buf][0][kv_swz(key, c)]) = rk[i];
-      *reinterpret_cast<u32x4*>(&lds[buf][1][kv_swz(key, c)]) = rv[i];
-    }
-  };
-  auto page_ok = [&](int pos) -> bool {
-    if (pos >= n_tok) return false;
-    const int p = bt[pos >> 4];
-    return p >= 0 && p < num_blocks;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  float Ms = -INFINITY, Ls = 0.0f;
-  f32x16 Os[4];
-#pragma unroll
-  for (int d = 0; d < 4; ++d)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) Os[d][v] = 0.0f;
+  // Segment result for the 16 outputs this thread owns: lane `lane`'s
+  // accumulator values v = wave + 4k, k = 0..15 (row li).  It is only live
+  // between rounds; a segment of more than one round (more than four chunks)
+  // parks it in its workspace slot while the next round's chunks run.
+  float Ms = -INFINITY, Ls = 0.0f, Os[16];
+  const int64_t slot = ((int64_t)r * Hkv + kvh) * nseg_max + seg;
+  float* slot_o = ws.part_o + slot * 4096;
+  float* slot_ml = ws.part_ml + slot * 128;
 
   const int first_chunk = tok_begin / kChunk;
   const int end_chunk = (tok_end + kChunk - 1) / kChunk;
-  const int n_subs = (end_chunk - first_chunk) * kSubsPerChunk;
-  int sub_i = 0;
-  load_sub(first_chunk * kChunk);
-  store_sub(0);
-  __syncthreads();
-  for (int c = first_chunk; c < end_chunk; ++c) {
+  for (int c0 = first_chunk; c0 < end_chunk; c0 += kWaves) {
+    const int c = c0 + wave;
     float mc = -INFINITY, lc = 0.0f;
     f32x16 oc[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
       for (int v = 0; v < 16; ++v) oc[d][v] = 0.0f;
-    for (int st = 0; st < kSubsPerChunk; ++st, ++sub_i) {
-      const int sub_base = c * kChunk + st * kSub;
-      const int buf = sub_i & 1;
-      const bool more = sub_i + 1 < n_subs;
-      if (more) load_sub(sub_base + kSub);
-      const unsigned char* Ks = lds[buf][0];
-      const unsigned char* Vs = lds[buf][1];
-      // S^T[key][row] for the 32 keys of this sub-tile
-      f32x16 s;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s[v] = 0.0f;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + kv_swz(li, 2 * t + g));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[t], s, 0, 0, 0);
-      }
-      const bool p0 = page_ok(sub_base), p1 = page_ok(sub_base + 16);
-      float x[16];
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int kk = 8 * (v >> 2) + 4 * g + (v & 3);
-        const int pos = sub_base + kk;
-        const bool ok = pos <= last_key && (kk < 16 ? p0 : p1);
-        x[v] = ok ? __fmul_rn(s[v], scale_log2) : -INFINITY;
-        tmax = fmaxf(tmax, x[v]);
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float mn = fmaxf(mc, tmax);
-      float alpha = 1.0f, lsum = 0.0f;
-      bf16x8 pb[2];
-      if (mn == -INFINITY) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pb[0][e] = (__bf16)0.0f;
-          pb[1][e] = (__bf16)0.0f;
+    if (c < end_chunk) {
+      // the chunk's 16 pages, one per lane 0..15, then read with readlane
+      int mypage = -1;
+      {
+        const int lp = c * 16 + lane;
+        if (lane < 16 && lp < n_pages) {
+          const int p = bt[lp];
+          mypage = (p >= 0 && p < num_blocks) ? p : -1;
         }
-      } else {
-        alpha = exp2f(mc - mn);
+      }
+      auto page = [&](int i) { return __builtin_amdgcn_readlane(mypage, i); };
+      const int base0 = c * kChunk;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // earlier LDS reads of the buffers are done
+      dma(k_cache, Ks, page(0), page(1));
+      dma(v_cache, Vs, page(0), page(1));
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // K of sub-tile 0 has landed
+      for (int st = 0; st < kSubsPerChunk; ++st) {
+        const int sub_base = base0 + st * kSub;
+        const int p0 = page(2 * st), p1 = page(2 * st + 1);
+        const bool more = st + 1 < kSubsPerChunk;
+        // S^T[key][row] for the 32 keys of this sub-tile
+        f32x16 s;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[v] = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + kv_swz(li, 2 * t + g));
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[t], s, 0, 0, 0);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // K reads done: refill the K buffer
+        if (more) dma(k_cache, Ks, page(2 * st + 2), page(2 * st + 3));
+        // every row sees every key of the sub-tile: no per-score mask
+        const bool all_visible = p0 >= 0 && p1 >= 0 && sub_base + kSub - 1 <= L;
+        float x[16];
+        float tmax = -INFINITY;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const float p = x[v] == -INFINITY ? 0.0f : exp2f(x[v] - mn);
-          lsum = __fadd_rn(lsum, p);
-          pb[v >> 3][v & 7] = (__bf16)p;
+          const int kk = 8 * (v >> 2) + 4 * g + (v & 3);
+          const bool ok = all_visible || (sub_base + kk <= last_key && (kk < 16 ? p0 : p1) >= 0);
+          x[v] = ok ? __fmul_rn(s[v], scale_log2) : -INFINITY;
+          tmax = fmaxf(tmax, x[v]);
         }
-      }
-      lsum = __fadd_rn(lsum, __shfl_xor(lsum, 32, 64));
-      lc = __fadd_rn(__fmul_rn(lc, alpha), lsum);
-      mc = mn;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) oc[d][v] = __fmul_rn(oc[d][v], alpha);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          // V^T fragment: dim 32d + li, keys matching the lane group's P values
-          bf16x8 va;
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const float mn = fmaxf(mc, tmax);
+        float alpha = 1.0f, lsum = 0.0f;
+        bf16x8 pb[2];
+        if (mn == -INFINITY) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const int kk = 16 * h + (e < 4 ? 4 * g + e : 8 + 4 * g + (e - 4));
-            const int dim = 32 * d + li;
-            const uint16_t bits = *reinterpret_cast<const uint16_t*>(Vs + kv_swz(kk, dim >> 3) + 2 * (dim & 7));
-            va[e] = __builtin_bit_cast(__bf16, bits);
+            pb[0][e] = (__bf16)0.0f;
+            pb[1][e] = (__bf16)0.0f;
           }
-          oc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[h], oc[d], 0, 0, 0);
+        } else {
+          alpha = exp2f(mc - mn);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const float p = x[v] == -INFINITY ? 0.0f : exp2f(x[v] - mn);
+            lsum = __fadd_rn(lsum, p);
+            pb[v >> 3][v & 7] = (__bf16)p;
+          }
+        }
+        lsum = __fadd_rn(lsum, __shfl_xor(lsum, 32, 64));
+        lc = __fadd_rn(__fmul_rn(lc, alpha), lsum);
+        mc = mn;
+        // V of this sub-tile has landed (the K refill, if any, is newer)
+        if (more)
+          asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        zero_missing(sub_base, p0, p1);
+        const bool rescale = __any(alpha != 1.0f);  // wave-uniform; x * 1 == x exactly
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          if (rescale) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) oc[d][v] = __fmul_rn(oc[d][v], alpha);
+          }
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            // V^T fragment: dim 32d + li, keys matching the lane group's P values
+            bf16x8 va;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int kk = 16 * h + (e < 4 ? 4 * g + e : 8 + 4 * g + (e - 4));
+              const int dim = 32 * d + li;
+              const uint16_t bits = *reinterpret_cast<const uint16_t*>(Vs + kv_swz(kk, dim >> 3) + 2 * (dim & 7));
+              va[e] = __builtin_bit_cast(__bf16, bits);
+            }
+            oc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[h], oc[d], 0, 0, 0);
+          }
+        }
+        if (more) {
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // V reads done: refill the V buffer
+          dma(v_cache, Vs, page(2 * st + 2), page(2 * st + 3));
+          asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // K of the next sub-tile has landed
         }
       }
-      if (more) store_sub(buf ^ 1);
-      __syncthreads();
     }
-    fold(Ms, Ls, Os, mc, lc, oc);
-  }
-
-  auto write_out = [&](float Lsum, const f32x16 (&O)[4]) {
-    if (!row_ok) return;
-    const float inv = Lsum > 0.0f ? __fdiv_rn(1.0f, Lsum) : 0.0f;
-    uint16_t* orow = out + orow_off;
+    // chunk partials meet in LDS (the staging buffer of each wave)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+    // values 0..31 of each lane go to the K buffer, 32..63 to the V buffer
+    float* pk = reinterpret_cast<float*>(lds_k[wave]);
+    float* pv = reinterpret_cast<float*>(lds_v[wave]);
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int dim = 32 * d + 8 * (v >> 2) + 4 * g + (v & 3);
-        orow[dim] = f2bf(__fmul_rn(O[d][v], inv));
+      for (int v = 0; v < 16; ++v) (d < 2 ? pk : pv)[((d & 1) * 16 + v) * 64 + lane] = oc[d][v];
+    lds_ml[wave][lane][0] = mc;
+    lds_ml[wave][lane][1] = lc;
+    __syncthreads();
+    if (c0 == first_chunk) {
+      Ms = -INFINITY;
+      Ls = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) Os[k] = 0.0f;
+    } else {  // resume the segment result parked after the previous round
+      Ms = slot_ml[lane * 2 + 0];
+      Ls = slot_ml[lane * 2 + 1];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) Os[k] = slot_o[tid + 256 * k];
+    }
+    for (int w = 0; w < kWaves; ++w) {  // ascending chunk order
+      const float* qk = reinterpret_cast<const float*>(lds_k[w]);
+      const float* qv = reinterpret_cast<const float*>(lds_v[w]);
+      float o[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int v = wave + 4 * k;
+        o[k] = (v < 32 ? qk : qv)[(v & 31) * 64 + lane];
       }
+      fold16(Ms, Ls, Os, lds_ml[w][lane][0], lds_ml[w][lane][1], o);
+    }
+    if (c0 + kWaves < end_chunk) {  // park for the next round (each thread reads back only its own values)
+#pragma unroll
+      for (int k = 0; k < 16; ++k) slot_o[tid + 256 * k] = Os[k];
+      if (wave == 0) {
+        slot_ml[lane * 2 + 0] = Ms;
+        slot_ml[lane * 2 + 1] = Ls;
+      }
+    }
+    __syncthreads();
+  }
+
+  // output element of value v = wave + 4k of lane `lane`
+  auto write_out = [&](float Lsum, const float (&O)[16]) {
+    if (!row_ok) return;
+    const float inv = Lsum > 0.0f ? __fdiv_rn(1.0f, Lsum) : 0.0f;
+    uint16_t* orow = out + (qtok * Hq + hq) * kHD;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int v = wave + 4 * k;
+      const int vv = v & 15;
+      const int dim = 32 * (v >> 4) + 8 * (vv >> 2) + 4 * g + (vv & 3);
+      orow[dim] = f2bf(__fmul_rn(O[k], inv));
+    }
   };
 
   if (nseg == 1) {
     write_out(Ls, Os);
     return;
   }
-  // segment result -> workspace; the last wave of this (request, KV head) folds
-  const int64_t slot = ((int64_t)r * Hkv + kvh) * nseg_max + seg;
-  float* po = ws.part_o + slot * 4096;
+  // segment result -> workspace; attn_combine_kernel folds the segments
 #pragma unroll
-  for (int d = 0; d < 4; ++d)
+  for (int k = 0; k < 16; ++k) slot_o[tid + 256 * k] = Os[k];
+  if (wave == 0) {
+    slot_ml[lane * 2 + 0] = Ms;
+    slot_ml[lane * 2 + 1] = Ls;
+  }
+}
+
+// Second pass for requests with more than one segment: left-fold the segment
+// results in ascending order (the same fold as above, element by element) and
+// write the output.  One workgroup per (KV head, request); thread t owns the
+// same 16 outputs as thread t of the first pass.
+__global__ __launch_bounds__(256) void attn_combine_kernel(const int32_t* __restrict__ ctx,
+                                                           uint16_t* __restrict__ out, int q_len, int Hq,
+                                                           int Hkv, int max_blocks, int seg_tokens, int nseg_max,
+                                                           AttnWs ws) {
+  const int kvh = blockIdx.x, r = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
+  const int G = Hq / Hkv, nrows = q_len * G;
+  const int n_tok = min(ctx[r] + q_len, max_blocks * 16);
+  const int nseg = (n_tok + seg_tokens - 1) / seg_tokens;
+  if (nseg <= 1 || li >= nrows) return;  // single segment: written by the first pass
+  const int jq = li / G, hq = kvh * G + li % G;
+  float M = -INFINITY, Lt = 0.0f, O[16];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) po[(d * 16 + v) * 64 + lane] = Os[d][v];
-  ws.part_ml[slot * 128 + lane * 2 + 0] = Ms;
-  ws.part_ml[slot * 128 + lane * 2 + 1] = Ls;
-  __threadfence();
-  unsigned prev = 0;
-  unsigned* cnt = ws.counters + (int64_t)r * Hkv + kvh;
-  if (lane == 0) prev = atomicAdd(cnt, 1u);
-  prev = __shfl(prev, 0, 64);
-  if (prev != (unsigned)(nseg - 1)) return;
-  __threadfence();
-  float M = -INFINITY, Lt = 0.0f;
-  f32x16 O[4];
-#pragma unroll
-  for (int d = 0; d < 4; ++d)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) O[d][v] = 0.0f;
+  for (int k = 0; k < 16; ++k) O[k] = 0.0f;
   for (int s2 = 0; s2 < nseg; ++s2) {
     const int64_t sl = ((int64_t)r * Hkv + kvh) * nseg_max + s2;
-    const float* p2 = ws.part_o + sl * 4096;
-    f32x16 o2[4];
+    float o2[16];
 #pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) o2[d][v] = __builtin_nontemporal_load(p2 + (d * 16 + v) * 64 + lane);
-    const float m2 = __builtin_nontemporal_load(ws.part_ml + sl * 128 + lane * 2 + 0);
-    const float l2 = __builtin_nontemporal_load(ws.part_ml + sl * 128 + lane * 2 + 1);
-    fold(M, Lt, O, m2, l2, o2);
+    for (int k = 0; k < 16; ++k) o2[k] = __builtin_nontemporal_load(ws.part_o + sl * 4096 + tid + 256 * k);
+    const float m2 = ws.part_ml[sl * 128 + lane * 2 + 0];
+    const float l2 = ws.part_ml[sl * 128 + lane * 2 + 1];
+    fold16(M, Lt, O, m2, l2, o2);
   }
-  write_out(Lt, O);
-  if (lane == 0) atomicExch(cnt, 0u);
+  const float inv = Lt > 0.0f ? __fdiv_rn(1.0f, Lt) : 0.0f;
+  uint16_t* orow = out + (((int64_t)r * q_len + jq) * Hq + hq) * kHD;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int v = wave + 4 * k;
+    const int vv = v & 15;
+    orow[32 * (v >> 4) + 8 * (vv >> 2) + 4 * g + (vv & 3)] = f2bf(__fmul_rn(O[k], inv));
+  }
 }
 
 // fp32 path: one wave per (query row, query head, request).  Same chunking:
@@ -394,14 +497,16 @@ static biv_status launch_attn_bf16(const char* who, const void* q, int64_t q_str
   const int nseg_max = (int)cdiv((int64_t)max_blocks * 16, seg_tokens);
   BIV_REQUIRE(nseg_max <= 0x7fffffff, "%s: too many segments", who);
   AttnWs ws;
-  unsigned char* base = static_cast<unsigned char*>(workspace);
-  ws.counters = reinterpret_cast<unsigned*>(base);
-  ws.part_o = reinterpret_cast<float*>(base + attn_counter_bytes(R, Hkv));
+  ws.part_o = static_cast<float*>(workspace);
   ws.part_ml = ws.part_o + (size_t)R * Hkv * nseg_max * 4096;
-  hipLaunchKernelGGL(attn_bf16_kernel, dim3(nseg_max, Hkv, R), dim3(64), 0, s, static_cast<const uint16_t*>(q), q_stride,
+  hipLaunchKernelGGL(attn_bf16_kernel, dim3(nseg_max, Hkv, R), dim3(64 * kWaves), 0, s, static_cast<const uint16_t*>(q), q_stride,
                      static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache), block_table, ctx,
                      static_cast<uint16_t*>(out), q_len, Hq, Hkv, max_blocks, num_blocks, scale * kLog2e,
                      seg_tokens, nseg_max, ws);
+  biv_status st = launched(who);
+  if (st != BIV_OK || nseg_max <= 1) return st;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(Hkv, R), dim3(256), 0, s, ctx, static_cast<uint16_t*>(out), q_len,
+                     Hq, Hkv, max_blocks, seg_tokens, nseg_max, ws);
   return launched(who);
 }
 
@@ -411,7 +516,7 @@ extern "C" size_t biv_attn_workspace_bytes(int R, int Hkv, int max_blocks, int s
   using namespace biv;
   if (R <= 0 || Hkv <= 0 || max_blocks <= 0 || seg_tokens <= 0) return 0;
   const size_t nseg = (size_t)cdiv((int64_t)max_blocks * 16, seg_tokens);
-  return attn_counter_bytes(R, Hkv) + (size_t)R * Hkv * nseg * (4096 + 128) * sizeof(float);
+  return (size_t)R * Hkv * nseg * (4096 + 128) * sizeof(float);
 }
 
 extern "C" biv_status attn_decode_bi(const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
