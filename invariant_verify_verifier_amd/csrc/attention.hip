@@ -51,25 +51,6 @@ struct AttnWs {
   float* part_ml;  // [slot][64 lanes][2]
 };
 
-// One gfx950 global_load_lds_dwordx4: lane i copies 16 bytes from
-// sbase + voff_i (sbase wave-uniform) to LDS bytes 16i..16i+15 after `dst`
-// (wave-uniform).  Issued as inline asm so that the compiler does not model
-// the LDS write: its own hazard tracking would wait for every outstanding
-// copy before any LDS read, which serialises the K/V pipeline.  Callers order
-// the copies with explicit vmcnt waits; loads the compiler issues itself stay
-// correct, since untracked copies only make its vmcnt waits stricter.  M0
-// (the LDS base of the copy) is not used by anything else in these kernels.
-__device__ __forceinline__ void lds_dma16(const void* sbase, unsigned voff, void* dst) {
-  const unsigned m0v =
-      __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)dst);
-  // readfirstlane yields a signed int: widen each half through uint32_t so
-  // the low half is zero-extended, never sign-extended into the high half
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)sbase);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((unsigned)((uintptr_t)sbase >> 32));
-  const uint64_t sb = (uint64_t)lo | ((uint64_t)hi << 32);
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb), "s"(m0v) : "memory");
-}
-
 // (M, L, O) <- fold((M, L, O), (m, l, o)) for the 16 outputs a thread owns.
 __device__ __forceinline__ void fold16(float& M, float& L, float (&O)[16], float m, float l, const float (&o)[16]) {
   const float mn = fmaxf(M, m);

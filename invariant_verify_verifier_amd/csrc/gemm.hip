@@ -135,6 +135,158 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(const uint16_t*
     }
 }
 
+// ----------------------------------------------------------------------------
+// bf16 path with K staged straight from HBM into a ring of LDS stages.
+//
+// The same per-element reduction as gemm_bf16_kernel -- one 32x32x16 MFMA
+// shape, k ascending in steps of 16, lanes 0-31 holding k 0..7 and lanes 32-63
+// k 8..15 of each step -- so the two kernels give identical bits, and a row's
+// bits never depend on M or on the tile it lands in.  K advances 64 per stage;
+// each stage's A (BM x 64) and B (BN x 64) tiles are copied HBM -> LDS by
+// global_load_lds_dwordx4 in 1 KiB windows of 8 rows x 128 B (whole 128-byte
+// lines: half-line rows move at roughly half the rate), STAGES - 1 stages in
+// flight ahead of the one being multiplied.  Four waves in a 2 x 2
+// arrangement own (BM/2) x (BN/2) outputs each.  The tile shape is chosen from
+// the weight shape (N) alone.
+constexpr int kDBK = 64;
+
+// 16-byte chunk c of LDS row r (128 B) is stored at position c ^ gemm_swz(r):
+// any 16 consecutive rows read at one logical chunk land in 16 distinct
+// 16-byte slots of the 256-byte span they share two by two, so a ds_read_b128
+// of 32 rows is bank-conflict free.
+__device__ __forceinline__ int gemm_swz(int r) { return (r >> 1) & 7; }
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding)
+template <int kN>
+__device__ __forceinline__ void vm_wait() {
+  __builtin_amdgcn_s_waitcnt((kN & 15) | (7 << 4) | (15 << 8) | (((kN >> 4) & 3) << 14));
+}
+template <int kPer, int kMax>
+__device__ __forceinline__ void vm_wait_stages(int ahead) {  // ahead in [0, kMax]
+  if constexpr (kMax == 0) {
+    vm_wait<0>();
+  } else {
+    if (ahead >= kMax)
+      vm_wait<kPer * kMax>();
+    else
+      vm_wait_stages<kPer, kMax - 1>(ahead);
+  }
+}
+
+template <int BM, int BN, int STAGES, int WAVES_M, int WAVES_N, int OUT_DT, int EPI, bool kSplit>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_kernel(const uint16_t* __restrict__ A,
+                                                       const uint16_t* __restrict__ B, void* C,
+                                                       float* __restrict__ partial, int M, int N, int K,
+                                                       int tilesM, int tilesN, int k_per_split) {
+  constexpr int ROW = kDBK * 2;  // 128 bytes of K per row per stage
+  constexpr int A_BYTES = BM * ROW;
+  constexpr int STAGE = (BM + BN) * ROW;
+  constexpr int WIN = (BM + BN) / 8;  // 1 KiB windows per stage
+  constexpr int NW = WAVES_M * WAVES_N;
+  static_assert(WIN % NW == 0, "windows must split evenly over the waves");
+  constexpr int PER_WAVE = WIN / NW;
+  static_assert(PER_WAVE * (STAGES - 2) <= 63, "vmcnt range");
+  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, FM = WM / 32, FN = WN / 32;
+  static_assert(FM >= 1 && FN >= 1, "wave tile must hold a 32x32 block");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[STAGES * STAGE];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int logical = xcd_remap(blockIdx.x, tilesM * tilesN);
+  const int m0 = (logical % tilesM) * BM;
+  const int n0 = (logical / tilesM) * BN;
+  const int k_begin = kSplit ? blockIdx.y * k_per_split : 0;
+  const int k_end = kSplit ? min(K, k_begin + k_per_split) : K;
+  const int nk = (k_end - k_begin) / kDBK;
+
+  // This wave's DMA windows: j = wave + NW q, A windows first, then B.  Window
+  // j holds rows 8j..8j+7 of its operand; lane -> row lane/8 of the window,
+  // LDS chunk lane%8 holding logical chunk (lane%8) ^ gemm_swz(8j + lane/8),
+  // which depends on j only through its parity (wave and q fix it).
+  const int r_in = lane >> 3;
+  const unsigned char* gbase[PER_WAVE];
+  unsigned voff[PER_WAVE];
+#pragma unroll
+  for (int q = 0; q < PER_WAVE; ++q) {
+    const int j = wave + NW * q;
+    const bool isA = j < BM / 8;
+    const int row0 = isA ? m0 + 8 * j : n0 + 8 * (j - BM / 8);
+    const int rows = isA ? M : N;
+    const int first = min(row0, rows - 1);       // window base row, in range
+    const int row = min(row0 + r_in, rows - 1);  // rows past the edge re-read the last row
+    const int c_log = (lane & 7) ^ gemm_swz(8 * j + r_in);
+    const uint16_t* src = isA ? A : B;
+    gbase[q] = reinterpret_cast<const unsigned char*>(src + (int64_t)first * K + k_begin);
+    voff[q] = (unsigned)((row - first) * K * 2 + c_log * 16);
+  }
+  auto issue = [&](int kt) {
+    unsigned char* slot = smem + (kt % STAGES) * STAGE;
+#pragma unroll
+    for (int q = 0; q < PER_WAVE; ++q)
+      lds_dma16(gbase[q] + (int64_t)kt * ROW, voff[q], slot + (wave + NW * q) * 1024);
+  };
+
+  // fragment offsets: row li of a 32-row block, logical chunk 2 ks + g
+  const int xs = gemm_swz(li);
+  int off[kDBK / 16];
+#pragma unroll
+  for (int ks = 0; ks < kDBK / 16; ++ks) off[ks] = li * ROW + 16 * ((2 * ks + g) ^ xs);
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st)
+    if (st < nk) issue(st);
+  for (int kt = 0; kt < nk; ++kt) {
+    vm_wait_stages<PER_WAVE, STAGES - 2>(min(STAGES - 2, nk - 1 - kt));  // stage kt has landed
+    __builtin_amdgcn_s_barrier();  // for every wave; and stage kt-1's slot is free
+    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
+    const unsigned char* As = smem + (kt % STAGES) * STAGE;
+    const unsigned char* Bs = As + A_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < kDBK / 16; ++ks) {
+      bf16x8 a[FM], b[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) a[i] = *reinterpret_cast<const bf16x8*>(As + (wm * WM + 32 * i) * ROW + off[ks]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) b[j] = *reinterpret_cast<const bf16x8*>(Bs + (wn * WN + 32 * j) * ROW + off[ks]);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // 32x32 accumulator layout: lane holds column li; value v is row 8(v/4) + 4g + v%4.
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = n0 + wn * WN + 32 * j + li;
+      if (n >= N) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = m0 + wm * WM + 32 * i + 8 * (v >> 2) + 4 * g + (v & 3);
+        if (m >= M) continue;
+        const int64_t idx = (int64_t)m * N + n;
+        const float x = acc[i][j][v];
+        if (kSplit) {
+          partial[(int64_t)blockIdx.y * M * N + idx] = x;
+        } else if (EPI == BIV_EPI_ACCUM) {
+          store_from_f32(C, idx, __fadd_rn(load_as_f32(C, idx, OUT_DT), x), OUT_DT);
+        } else {
+          store_from_f32(C, idx, x, OUT_DT);
+        }
+      }
+    }
+}
+
 // fp32 path: 64 x 64 tiles, K staged 16 at a time, each lane owns 4 x 4
 // outputs; every output is one fused multiply-add chain over k ascending.
 constexpr int kFT = 64, kFK = 16;
@@ -213,6 +365,38 @@ static void launch_bf16(const void* A, const void* B, void* C, float* partial, i
                      tilesM, tilesN, k_per_split);
 }
 
+// Tile of the staged kernel for a weight with N outputs (never depends on M).
+enum DmaTile { kTileL = 0, kTileS = 1, kTileT = 2 };
+#ifndef BIV_GEMM_L_TILE
+#define BIV_GEMM_L_TILE 256, 256, 2, 2, 4  // BM, BN, stages, waves along M, waves along N
+#endif
+static DmaTile dma_tile_for(int64_t N) {
+  if (N >= 16384) return kTileL;  // 256 x 256, 8 waves of 128 x 64, 2 stages (128 KiB LDS)
+  if (N >= 8192) return kTileS;   // 128 x 128, 2 stages (64 KiB, two per CU)
+  return kTileT;                  // 64 x 128, 3 stages (72 KiB, two per CU)
+}
+
+template <int BM, int BN, int STAGES, int WAVES_M, int WAVES_N, int OUT_DT, int EPI, bool kSplit>
+static void launch_dma_t(const void* A, const void* B, void* C, float* partial, int M, int N, int K, int splits,
+                         int k_per_split, hipStream_t s) {
+  const int tilesM = (int)cdiv(M, BM), tilesN = (int)cdiv(N, BN);
+  hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, STAGES, WAVES_M, WAVES_N, OUT_DT, EPI, kSplit>), dim3(tilesM * tilesN, splits),
+                     dim3(64 * WAVES_M * WAVES_N),
+                     0, s, static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), C, partial, M, N, K,
+                     tilesM, tilesN, k_per_split);
+}
+
+template <int OUT_DT, int EPI, bool kSplit>
+static void launch_dma(DmaTile t, const void* A, const void* B, void* C, float* partial, int M, int N, int K,
+                       int splits, int k_per_split, hipStream_t s) {
+  if (t == kTileL)
+    launch_dma_t<BIV_GEMM_L_TILE, OUT_DT, EPI, kSplit>(A, B, C, partial, M, N, K, splits, k_per_split, s);
+  else if (t == kTileS)
+    launch_dma_t<128, 128, 2, 2, 2, OUT_DT, EPI, kSplit>(A, B, C, partial, M, N, K, splits, k_per_split, s);
+  else
+    launch_dma_t<64, 128, 3, 2, 2, OUT_DT, EPI, kSplit>(A, B, C, partial, M, N, K, splits, k_per_split, s);
+}
+
 static biv_status check_gemm_args(const char* who, const void* A, const void* B, void* C, int64_t M, int64_t N,
                                   int64_t K, int out_dt, int epilogue) {
   BIV_REQUIRE(valid_dt(out_dt), "%s: bad out dtype %d", who, out_dt);
@@ -239,6 +423,18 @@ extern "C" biv_status gemm_bi(const void* A, const void* B, void* C, int64_t M, 
     BIV_REQUIRE(K % 8 == 0, "gemm_bi: bf16 path needs K %% 8 == 0 (K=%lld)", (long long)K);
     BIV_REQUIRE(aligned16(A) && aligned16(B), "gemm_bi: bf16 path needs 16-byte aligned A and B");
     BIV_REQUIRE(cdiv(M, kBM) * cdiv(N, kBN) <= 0x7fffffff, "gemm_bi: too many tiles");
+    BIV_REQUIRE((int64_t)K * 2 * 16 <= 0x7fffffff, "gemm_bi: K too large");
+    if (K % kDBK == 0) {  // staged kernel (same reduction, identical bits); chosen by K alone, never by M
+      const DmaTile t = dma_tile_for(N);
+      if (out_dt == BIV_BF16) {
+        if (epilogue == BIV_EPI_ACCUM) launch_dma<BIV_BF16, BIV_EPI_ACCUM, false>(t, A, B, C, nullptr, m, n, k, 1, k, s);
+        else launch_dma<BIV_BF16, BIV_EPI_STORE, false>(t, A, B, C, nullptr, m, n, k, 1, k, s);
+      } else {
+        if (epilogue == BIV_EPI_ACCUM) launch_dma<BIV_F32, BIV_EPI_ACCUM, false>(t, A, B, C, nullptr, m, n, k, 1, k, s);
+        else launch_dma<BIV_F32, BIV_EPI_STORE, false>(t, A, B, C, nullptr, m, n, k, 1, k, s);
+      }
+      return launched("gemm_bi/bf16-staged");
+    }
     if (out_dt == BIV_BF16) {
       if (epilogue == BIV_EPI_ACCUM) launch_bf16<BIV_BF16, BIV_EPI_ACCUM, false>(A, B, C, nullptr, m, n, k, 1, k, s);
       else launch_bf16<BIV_BF16, BIV_EPI_STORE, false>(A, B, C, nullptr, m, n, k, 1, k, s);
@@ -302,7 +498,10 @@ extern "C" biv_status gemm_splitk(const void* A, const void* B, void* C, int64_t
               "gemm_splitk: workspace needs %zu bytes", biv_splitk_workspace_bytes(M, N, sp));
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* part = static_cast<float*>(workspace);
-  launch_bf16<BIV_F32, BIV_EPI_STORE, true>(A, B, C, part, (int)M, (int)N, (int)K, sp, kps, s);
+  if (K % kDBK == 0)
+    launch_dma<BIV_F32, BIV_EPI_STORE, true>(dma_tile_for(N), A, B, C, part, (int)M, (int)N, (int)K, sp, kps, s);
+  else
+    launch_bf16<BIV_F32, BIV_EPI_STORE, true>(A, B, C, part, (int)M, (int)N, (int)K, sp, kps, s);
   st = launched("gemm_splitk/partials");
   if (st != BIV_OK) return st;
   const int64_t MN = M * N;
