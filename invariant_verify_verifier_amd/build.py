@@ -26,6 +26,12 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-ffp-contract=fast",
 ]
+# Per-source extras.  The attention kernel runs one wave per SIMD and also
+# rescales and folds its MFMA accumulators with vector ALU code: keeping MFMA
+# results in ordinary VGPRs avoids copying them to and from AGPRs every step.
+EXTRA = {
+    "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def sources():
@@ -34,7 +40,7 @@ def sources():
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ_DIR, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{p.stdout}\n{p.stderr}")

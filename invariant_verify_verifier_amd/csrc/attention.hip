@@ -40,59 +40,82 @@ constexpr int kHD = 128;                 // head dim of the MFMA path
 constexpr int kSub = 32;                 // keys per sub-tile
 constexpr int kChunk = BIV_ATTN_CHUNK_TOKENS;
 constexpr int kSubsPerChunk = kChunk / kSub;
-constexpr int kWaves = 4;                // waves per workgroup = chunks per round
-constexpr int kStage = kSub * kHD * 2 * 2;  // 16 KiB: K and V of one sub-tile
+constexpr int kSlot = kSub * kHD * 2;    // 8 KiB: K or V of one sub-tile
+constexpr int kRing = 5;                 // LDS slots per wave (40 KiB: four waves fill a CU's 160 KiB)
+constexpr int kPagesPerWin = 64;         // page ids held in one register (lane i: page i of the window)
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.0f;            // max drift (log2) before the accumulators are rescaled
 
-__device__ __forceinline__ int kv_swz(int key, int chunk) { return key * 256 + ((chunk ^ (key & 7)) << 4); }
+// 2^x with the hardware instruction (v_exp_f32): exact at 0 and -inf; a
+// result below the normal range is flushed to zero.
+__device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Position of 16-byte piece c of key row k (256 bytes) in LDS is c ^ kv_swz(k).
+// K reads (16 lanes = 16 consecutive keys, one piece each) and V transpose
+// reads (4 consecutive keys x 4 consecutive pieces per 32 lanes) both land on
+// distinct bank groups.
+__device__ __forceinline__ int kv_swz(int k) { return ((k & 3) << 2) | ((k >> 2) & 3); }
 
 struct AttnWs {
-  float* part_o;   // [slot][4096]: element t + 256 k of thread t
+  float* part_o;   // [slot][64 values][64 lanes]
   float* part_ml;  // [slot][64 lanes][2]
 };
 
-// (M, L, O) <- fold((M, L, O), (m, l, o)) for the 16 outputs a thread owns.
-__device__ __forceinline__ void fold16(float& M, float& L, float (&O)[16], float m, float l, const float (&o)[16]) {
+// Wait until at most 8n direct-to-LDS copies (n loads) are outstanding.
+__device__ __forceinline__ void wait_loads_after(int n) {
+  switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(32)" ::: "memory"); break;
+  }
+}
+
+// (M, L, O) <- fold((M, L, O), (m, l, o)) over N outputs.
+template <int N>
+__device__ __forceinline__ void fold_into(float& M, float& L, float* O, float m, float l, const float* o) {
   const float mn = fmaxf(M, m);
   if (mn == -INFINITY) return;  // both empty
   const float a = exp2f(M - mn);  // 0 when M == -inf, exactly 1 when M == mn
   const float b = exp2f(m - mn);
   L = __fadd_rn(__fmul_rn(L, a), __fmul_rn(l, b));
 #pragma unroll
-  for (int k = 0; k < 16; ++k) O[k] = __fadd_rn(__fmul_rn(O[k], a), __fmul_rn(o[k], b));
+  for (int k = 0; k < N; ++k) O[k] = __fadd_rn(__fmul_rn(O[k], a), __fmul_rn(o[k], b));
   M = mn;
 }
 
-__global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
+// One wave per (segment, KV head, request).  The wave streams the K and V
+// sub-tiles of its segment through a ring of kRing 8 KiB LDS slots in the
+// order K0 V0 K1 V1 ...; a slot is refilled with the load kRing places later
+// as soon as it has been read, so up to kRing loads are in flight at once.
+// Lane (li, g) owns query row li of the KV head's 32-row block: it computes
+// S^T = K Q^T and O^T = V^T P^T with the 32x32x16 bf16 MFMA (its column),
+// keeps the chunk partial (m, l, o) and the segment result (M, L, O) of its
+// row in registers, and folds each finished chunk into the segment result.
+__global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx,
     uint16_t* __restrict__ out, int q_len, int Hq, int Hkv, int max_blocks, int num_blocks, float scale_log2,
     int seg_tokens, int nseg_max, AttnWs ws) {
-  // per wave: staging of one sub-tile's K and V (separate arrays, so the
-  // compiler tracks the direct-to-LDS loads of each apart), reused for the
-  // wave's chunk partial
-  __shared__ __attribute__((aligned(16))) unsigned char lds_k[kWaves][kStage / 2];
-  __shared__ __attribute__((aligned(16))) unsigned char lds_v[kWaves][kStage / 2];
-  __shared__ float lds_ml[kWaves][64][2];
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kRing * kSlot];
   const int seg = blockIdx.x, kvh = blockIdx.y, r = blockIdx.z;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
+  const int lane = threadIdx.x, g = lane >> 5, li = lane & 31;
   const int G = Hq / Hkv, nrows = q_len * G;
-  const int L = ctx[r];
-  const int n_tok = min(L + q_len, max_blocks * 16);
-  const int nseg = (n_tok + seg_tokens - 1) / seg_tokens;
-  if (seg >= nseg) return;
-  const int tok_begin = seg * seg_tokens;
-  const int tok_end = min(tok_begin + seg_tokens, n_tok);
   const int32_t* bt = block_table + (int64_t)r * max_blocks;
+  const int page0 = seg * (seg_tokens >> 4);  // first page of the segment
 
-  // this lane's query row (MFMA column li) and its last visible key
-  const int rho = li;
-  const bool row_ok = rho < nrows;
-  const int jq = row_ok ? rho / G : 0;
-  const int hq = kvh * G + (row_ok ? rho % G : 0);
-  const int last_key = row_ok ? L + jq : -1;
+  // The context length, the segment's first page window and the queries are
+  // loaded together: none depends on another, and the copies of the first
+  // sub-tiles can only start once all three have landed.
+  const int L = ctx[r];
+  int bt_w0 = -1;
+  if (page0 + lane < max_blocks) bt_w0 = bt[page0 + lane];
+  // this lane's query row (MFMA column li)
+  const bool row_ok = li < nrows;
+  const int jq = row_ok ? li / G : 0;
+  const int hq = kvh * G + (row_ok ? li % G : 0);
   const int64_t qtok = (int64_t)r * q_len + jq;
-
   bf16x8 bq[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
@@ -104,270 +127,284 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
     }
   }
 
-  unsigned char* Ks = lds_k[wave];
-  unsigned char* Vs = lds_v[wave];
+  const int n_tok = min(L + q_len, max_blocks * 16);
+  const int nseg = (n_tok + seg_tokens - 1) / seg_tokens;
+  if (seg >= nseg) return;
+  const int tok_begin = seg * seg_tokens;  // a multiple of kChunk
+  const int tok_end = min(tok_begin + seg_tokens, n_tok);
+  const int nsub = (tok_end - tok_begin + kSub - 1) / kSub;
+  const int total = 2 * nsub;  // loads: K(s) = 2s, V(s) = 2s + 1
   const int n_pages = (n_tok + 15) >> 4;
-  // Staging of 32 keys of K (or V) straight from HBM into LDS (gfx950
-  // global_load_lds_dwordx4: no registers, lane i writes bytes 16i..16i+15 of
-  // the instruction's 1 KiB window).  Instruction i covers keys 4i..4i+3, all
-  // in one page; the XOR swizzle of the LDS layout is applied by choosing
-  // which 16-byte chunk of its key each lane fetches.  Keys of a missing page
-  // are fetched from page 0 (in bounds); their values, and those of positions
-  // past the request's last one, are zeroed after landing: a masked key must
-  // contribute exactly nothing, whatever its slot holds.  Each call issues 8
-  // loads, counted by vmcnt in issue order.
-  // byte offset of lane's 16-byte piece within a 4-key, 1 KiB window of a
-  // page: key 4i + lane/16 (row), 16-byte chunk (lane%16) ^ (key%8) (the
-  // swizzle); key%8 = 4(i%2) + lane/16, so two variants cover every i
-  const unsigned voff_even = 256u * (lane >> 4) + 16u * ((lane & 15) ^ (lane >> 4));
-  const unsigned voff_odd = 256u * (lane >> 4) + 16u * ((lane & 15) ^ (4 + (lane >> 4)));
-  auto dma = [&](const uint16_t* cache, unsigned char* dst, int p0, int p1) {
-    const uint16_t* b0 = cache + ((int64_t)(p0 >= 0 ? p0 : 0) * Hkv + kvh) * 16 * kHD;
-    const uint16_t* b1 = cache + ((int64_t)(p1 >= 0 ? p1 : 0) * Hkv + kvh) * 16 * kHD;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const unsigned char* base = reinterpret_cast<const unsigned char*>(i < 4 ? b0 : b1) + 1024 * (i & 3);
-      lds_dma16(base, (i & 1) ? voff_odd : voff_even, dst + 1024 * i);
-    }
+  const int last_key = row_ok ? L + jq : -1;  // this row's last visible key
+
+  // page ids of a 64-page window of the segment (-1: missing or out of range)
+  auto window_ids = [&](int w, int raw) {
+    const int lp = page0 + kPagesPerWin * w + lane;
+    return (lp < n_pages && raw >= 0 && raw < num_blocks) ? raw : -1;
   };
-  auto zero_missing = [&](int sub_base, int p0, int p1) {
-    if (p0 >= 0 && p1 >= 0 && sub_base + kSub <= n_tok) return;  // wave-uniform
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int key = 4 * i + (lane >> 4);
-      const bool ok = (i < 4 ? p0 : p1) >= 0 && sub_base + key < n_tok;
-      if (!ok) *reinterpret_cast<u32x4*>(Vs + 1024 * i + 16 * lane) = zero;  // row of key 4i + lane/16
+  auto load_window = [&](int w) {
+    const int lp = page0 + kPagesPerWin * w + lane;
+    return window_ids(w, lp < n_pages ? bt[lp] : -1);
+  };
+  int mypage = window_ids(0, bt_w0);
+  int win = 0;
+  uint32_t valid_q = 0;  // bits 2(s%16), 2(s%16)+1: pages of sub-tile s present
+
+  // Direct-to-LDS copy of one sub-tile (32 keys) of K or V: 8 copies of
+  // 4 keys (1 KiB) each; lane i writes LDS bytes 16i..16i+15 of its copy's
+  // window, i.e. row 4c + i/16, position i%16, so it fetches piece
+  // (i%16) ^ kv_swz(row) of that key.  kv_swz(4c + i/16) = 4(i/16) + c%4.
+  const unsigned voff0 = 256u * (lane >> 4) + 16u * ((lane & 15) ^ (4 * (lane >> 4)));
+  auto issue = [&](int j, int slot) {
+    const int s = j >> 1;
+    if (!(j & 1) && (s >> 5) != win) {  // K of the first sub-tile of a new window
+      win = s >> 5;
+      mypage = load_window(win);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int p0 = __builtin_amdgcn_readlane(mypage, (2 * s) & 63);
+    const int p1 = __builtin_amdgcn_readlane(mypage, (2 * s + 1) & 63);
+    if (!(j & 1)) {
+      const int sh = 2 * (s & 15);
+      valid_q = (valid_q & ~(3u << sh)) | ((uint32_t)(p0 >= 0) << sh) | ((uint32_t)(p1 >= 0) << (sh + 1));
+    }
+    const uint16_t* cache = (j & 1) ? v_cache : k_cache;
+    const unsigned char* b0 =
+        reinterpret_cast<const unsigned char*>(cache + ((int64_t)(p0 >= 0 ? p0 : 0) * Hkv + kvh) * 16 * kHD);
+    const unsigned char* b1 =
+        reinterpret_cast<const unsigned char*>(cache + ((int64_t)(p1 >= 0 ? p1 : 0) * Hkv + kvh) * 16 * kHD);
+    unsigned char* dst = ring + slot * kSlot;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lds_dma16((i < 4 ? b0 : b1) + 1024 * (i & 3), voff0 ^ (16u * (i & 3)), dst + 1024 * i);
   };
 
-  // Segment result for the 16 outputs this thread owns: lane `lane`'s
-  // accumulator values v = wave + 4k, k = 0..15 (row li).  It is only live
-  // between rounds; a segment of more than one round (more than four chunks)
-  // parks it in its workspace slot while the next round's chunks run.
-  float Ms = -INFINITY, Ls = 0.0f, Os[16];
-  const int64_t slot = ((int64_t)r * Hkv + kvh) * nseg_max + seg;
-  float* slot_o = ws.part_o + slot * 4096;
-  float* slot_ml = ws.part_ml + slot * 128;
-
-  const int first_chunk = tok_begin / kChunk;
-  const int end_chunk = (tok_end + kChunk - 1) / kChunk;
-  for (int c0 = first_chunk; c0 < end_chunk; c0 += kWaves) {
-    const int c = c0 + wave;
-    float mc = -INFINITY, lc = 0.0f;
-    f32x16 oc[4];
+  // K read of step t: piece 2t + g of key li at position (2t + g) ^ kv_swz(li)
+  const int k_off = li * 256 + 16 * (g ^ kv_swz(li));  // XOR 32t selects step t
+  // V transpose reads.  In each group of 16 lanes, source lane s points at
+  // dims base + 4(s%4) .. +3 of key kb + s/4; the read hands lane i the
+  // 4 keys kb .. kb+3 of dim base + i.  Group 2g + half covers dims
+  // 32d + 16 half .. +15 and keys kb = 16h + 8u + 4g (u: first or second
+  // four of the lane's eight), matching the key order of the P operand.
+  int v_off[4][2];
+  {
+    const int sl = lane & 15, half = (lane >> 4) & 1;
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) oc[d][v] = 0.0f;
-    if (c < end_chunk) {
-      // the chunk's 16 pages, one per lane 0..15, then read with readlane
-      int mypage = -1;
-      {
-        const int lp = c * 16 + lane;
-        if (lane < 16 && lp < n_pages) {
-          const int p = bt[lp];
-          mypage = (p >= 0 && p < num_blocks) ? p : -1;
-        }
+      for (int u = 0; u < 2; ++u) {
+        const int kk = 8 * u + 4 * g + (sl >> 2);  // + 16h (an immediate)
+        const int c = 4 * d + 2 * half + ((sl & 3) >> 1);
+        v_off[d][u] = kk * 256 + 16 * (c ^ kv_swz(kk)) + 8 * (sl & 1);
       }
-      auto page = [&](int i) { return __builtin_amdgcn_readlane(mypage, i); };
-      const int base0 = c * kChunk;
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // earlier LDS reads of the buffers are done
-      dma(k_cache, Ks, page(0), page(1));
-      dma(v_cache, Vs, page(0), page(1));
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // K of sub-tile 0 has landed
-      for (int st = 0; st < kSubsPerChunk; ++st) {
-        const int sub_base = base0 + st * kSub;
-        const int p0 = page(2 * st), p1 = page(2 * st + 1);
-        const bool more = st + 1 < kSubsPerChunk;
-        // S^T[key][row] for the 32 keys of this sub-tile
-        f32x16 s;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) s[v] = 0.0f;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + kv_swz(li, 2 * t + g));
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[t], s, 0, 0, 0);
-        }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // K reads done: refill the K buffer
-        if (more) dma(k_cache, Ks, page(2 * st + 2), page(2 * st + 3));
-        // every row sees every key of the sub-tile: no per-score mask
-        const bool all_visible = p0 >= 0 && p1 >= 0 && sub_base + kSub - 1 <= L;
-        float x[16];
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int kk = 8 * (v >> 2) + 4 * g + (v & 3);
-          const bool ok = all_visible || (sub_base + kk <= last_key && (kk < 16 ? p0 : p1) >= 0);
-          x[v] = ok ? __fmul_rn(s[v], scale_log2) : -INFINITY;
-          tmax = fmaxf(tmax, x[v]);
-        }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float mn = fmaxf(mc, tmax);
-        float alpha = 1.0f, lsum = 0.0f;
-        bf16x8 pb[2];
-        if (mn == -INFINITY) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            pb[0][e] = (__bf16)0.0f;
-            pb[1][e] = (__bf16)0.0f;
-          }
-        } else {
-          alpha = exp2f(mc - mn);
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const float p = x[v] == -INFINITY ? 0.0f : exp2f(x[v] - mn);
-            lsum = __fadd_rn(lsum, p);
-            pb[v >> 3][v & 7] = (__bf16)p;
-          }
-        }
-        lsum = __fadd_rn(lsum, __shfl_xor(lsum, 32, 64));
-        lc = __fadd_rn(__fmul_rn(lc, alpha), lsum);
-        mc = mn;
-        // V of this sub-tile has landed (the K refill, if any, is newer)
-        if (more)
-          asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        zero_missing(sub_base, p0, p1);
-        const bool rescale = __any(alpha != 1.0f);  // wave-uniform; x * 1 == x exactly
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          if (rescale) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) oc[d][v] = __fmul_rn(oc[d][v], alpha);
-          }
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            // V^T fragment: dim 32d + li, keys matching the lane group's P values
-            bf16x8 va;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int kk = 16 * h + (e < 4 ? 4 * g + e : 8 + 4 * g + (e - 4));
-              const int dim = 32 * d + li;
-              const uint16_t bits = *reinterpret_cast<const uint16_t*>(Vs + kv_swz(kk, dim >> 3) + 2 * (dim & 7));
-              va[e] = __builtin_bit_cast(__bf16, bits);
-            }
-            oc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[h], oc[d], 0, 0, 0);
-          }
-        }
-        if (more) {
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // V reads done: refill the V buffer
-          dma(v_cache, Vs, page(2 * st + 2), page(2 * st + 3));
-          asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // K of the next sub-tile has landed
-        }
-      }
-    }
-    // chunk partials meet in LDS (the staging buffer of each wave)
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __syncthreads();
-    // values 0..31 of each lane go to the K buffer, 32..63 to the V buffer
-    float* pk = reinterpret_cast<float*>(lds_k[wave]);
-    float* pv = reinterpret_cast<float*>(lds_v[wave]);
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) (d < 2 ? pk : pv)[((d & 1) * 16 + v) * 64 + lane] = oc[d][v];
-    lds_ml[wave][lane][0] = mc;
-    lds_ml[wave][lane][1] = lc;
-    __syncthreads();
-    if (c0 == first_chunk) {
-      Ms = -INFINITY;
-      Ls = 0.0f;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) Os[k] = 0.0f;
-    } else {  // resume the segment result parked after the previous round
-      Ms = slot_ml[lane * 2 + 0];
-      Ls = slot_ml[lane * 2 + 1];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) Os[k] = slot_o[tid + 256 * k];
-    }
-    for (int w = 0; w < kWaves; ++w) {  // ascending chunk order
-      const float* qk = reinterpret_cast<const float*>(lds_k[w]);
-      const float* qv = reinterpret_cast<const float*>(lds_v[w]);
-      float o[16];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int v = wave + 4 * k;
-        o[k] = (v < 32 ? qk : qv)[(v & 31) * 64 + lane];
-      }
-      fold16(Ms, Ls, Os, lds_ml[w][lane][0], lds_ml[w][lane][1], o);
-    }
-    if (c0 + kWaves < end_chunk) {  // park for the next round (each thread reads back only its own values)
-#pragma unroll
-      for (int k = 0; k < 16; ++k) slot_o[tid + 256 * k] = Os[k];
-      if (wave == 0) {
-        slot_ml[lane * 2 + 0] = Ms;
-        slot_ml[lane * 2 + 1] = Ls;
-      }
-    }
-    __syncthreads();
   }
 
-  // output element of value v = wave + 4k of lane `lane`
-  auto write_out = [&](float Lsum, const float (&O)[16]) {
+  // Q and the page ids have landed.  Issued as the builtin, which the
+  // compiler's own wait tracking sees: it then knows no load of its own is
+  // pending in the loop below and inserts no wait there that would also
+  // drain the ring of copies.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  // prologue: the first kRing loads
+  const int n_pro = min(kRing, total);
+  for (int j = 0; j < n_pro; ++j) issue(j, j);
+
+  float Ms = -INFINITY, Ls = 0.0f, Os[64];
+#pragma unroll
+  for (int k = 0; k < 64; ++k) Os[k] = 0.0f;
+  float mc = -INFINITY, lc = 0.0f;
+  f32x16 oc[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) oc[d][v] = 0.0f;
+
+  int sk = 0, sv = 1;  // slots of K(s) and V(s)
+  for (int s = 0; s < nsub; ++s) {
+    const int sub_base = tok_begin + s * kSub;
+    const uint32_t vb = valid_q >> (2 * (s & 15));
+    const bool ok0 = vb & 1u, ok1 = vb & 2u;
+    // ---- S^T = K Q^T
+    wait_loads_after(min(kRing - 1, total - 1 - 2 * s));
+    const unsigned char* Ks = ring + sk * kSlot;
+    f32x16 sacc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sacc[v] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + (k_off ^ (32 * t)));
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[t], sacc, 0, 0, 0);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // K slot read: refill it
+    if (2 * s + kRing < total) issue(2 * s + kRing, sk);
+    // ---- softmax statistics of the sub-tile (log2 domain)
+    // score v of the lane is key kk = 8(v/4) + 4g + v%4 of the sub-tile; it
+    // is visible when kk <= last_key - sub_base and its page is present
+    float x[16];
+    if (ok0 && ok1 && sub_base + kSub - 1 <= L) {  // wave-uniform: every row sees every key
+#pragma unroll
+      for (int v = 0; v < 16; ++v) x[v] = __fmul_rn(sacc[v], scale_log2);
+    } else {
+      const int lim = last_key - sub_base - 4 * g;  // compare 8(v/4) + v%4 against it
+      const int lim_lo = ok0 ? lim : -1, lim_hi = ok1 ? lim : -1;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const bool ok = 8 * (v >> 2) + (v & 3) <= (v < 8 ? lim_lo : lim_hi);
+        x[v] = ok ? __fmul_rn(sacc[v], scale_log2) : -INFINITY;
+      }
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, x[v]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    // The row's reference max moves only when a score exceeds it by more
+    // than kLazy (log2 units), so p <= 2^kLazy and the accumulators are
+    // rescaled rarely; the result is the same softmax, and the decision
+    // depends on the row's own scores alone.
+    const float mn = (mc == -INFINITY || tmax > mc + kLazy) ? tmax : mc;
+    float alpha = 1.0f, lsum = 0.0f;
+    bf16x8 pb[2];
+    if (mn == -INFINITY) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pb[0][e] = (__bf16)0.0f;
+        pb[1][e] = (__bf16)0.0f;
+      }
+    } else {
+      alpha = mc == -INFINITY ? 0.0f : exp2_raw(mc - mn);  // exactly 1 when mn == mc
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float p = exp2_raw(x[v] - mn);  // masked: exp2(-inf) = 0
+        lsum = __fadd_rn(lsum, p);
+        pb[v >> 3][v & 7] = (__bf16)p;
+      }
+    }
+    lsum = __fadd_rn(lsum, __shfl_xor(lsum, 32, 64));
+    lc = __fadd_rn(__fmul_rn(lc, alpha), lsum);
+    mc = mn;
+    // ---- O^T += V^T P^T
+    wait_loads_after(min(kRing - 1, total - 2 - 2 * s));
+    unsigned char* Vs = ring + sv * kSlot;
+    if (!(ok0 && ok1 && sub_base + kSub <= n_tok)) {  // wave-uniform: zero V rows of masked keys
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int key = 4 * i + (lane >> 4);
+        const bool ok = (i < 4 ? ok0 : ok1) && sub_base + key < n_tok;
+        if (!ok) *reinterpret_cast<u32x4*>(Vs + 1024 * i + 16 * lane) = zero;  // row of key 4i + lane/16
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    // wave-uniform; rows that keep their max multiply by exactly 1, and a
+    // chunk's first visible sub-tile finds its accumulators still zero
+    const bool rescale = __any(alpha != 1.0f && alpha != 0.0f);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      if (rescale) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oc[d][v] = __fmul_rn(oc[d][v], alpha);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4*)(Vs + v_off[d][0] + 4096 * h));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4*)(Vs + v_off[d][1] + 4096 * h));
+        const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        oc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[h], oc[d], 0, 0, 0);
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // V slot read: refill it
+    if (2 * s + 1 + kRing < total) issue(2 * s + 1 + kRing, sv);
+    sk = sk + 2 >= kRing ? sk + 2 - kRing : sk + 2;
+    sv = sv + 2 >= kRing ? sv + 2 - kRing : sv + 2;
+    // ---- end of a chunk: fold its partial into the segment result (ascending)
+    if ((s + 1) % kSubsPerChunk == 0 || s + 1 == nsub) {
+      float o[64];
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[16 * d + v] = oc[d][v];
+      fold_into<64>(Ms, Ls, Os, mc, lc, o);
+      mc = -INFINITY;
+      lc = 0.0f;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oc[d][v] = 0.0f;
+    }
+  }
+
+  // value k = 16d + v of lane (li, g): dim 32d + 8(v/4) + 4g + v%4 of row li
+  if (nseg == 1) {
     if (!row_ok) return;
-    const float inv = Lsum > 0.0f ? __fdiv_rn(1.0f, Lsum) : 0.0f;
+    const float inv = Ls > 0.0f ? __fdiv_rn(1.0f, Ls) : 0.0f;
     uint16_t* orow = out + (qtok * Hq + hq) * kHD;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int v = wave + 4 * k;
-      const int vv = v & 15;
-      const int dim = 32 * (v >> 4) + 8 * (vv >> 2) + 4 * g + (vv & 3);
-      orow[dim] = f2bf(__fmul_rn(O[k], inv));
+    for (int k4 = 0; k4 < 16; ++k4) {
+      const int d = k4 >> 2, v0 = 4 * (k4 & 3);
+      uint32_t w0 = (uint32_t)f2bf(__fmul_rn(Os[16 * d + v0 + 0], inv)) |
+                    ((uint32_t)f2bf(__fmul_rn(Os[16 * d + v0 + 1], inv)) << 16);
+      uint32_t w1 = (uint32_t)f2bf(__fmul_rn(Os[16 * d + v0 + 2], inv)) |
+                    ((uint32_t)f2bf(__fmul_rn(Os[16 * d + v0 + 3], inv)) << 16);
+      *reinterpret_cast<uint2*>(orow + 32 * d + 8 * (k4 & 3) + 4 * g) = make_uint2(w0, w1);
     }
-  };
-
-  if (nseg == 1) {
-    write_out(Ls, Os);
     return;
   }
   // segment result -> workspace; attn_combine_kernel folds the segments
+  const int64_t slot = ((int64_t)r * Hkv + kvh) * nseg_max + seg;
+  float* slot_o = ws.part_o + slot * 4096;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) slot_o[tid + 256 * k] = Os[k];
-  if (wave == 0) {
-    slot_ml[lane * 2 + 0] = Ms;
-    slot_ml[lane * 2 + 1] = Ls;
-  }
+  for (int k = 0; k < 64; ++k) slot_o[k * 64 + lane] = Os[k];
+  ws.part_ml[slot * 128 + lane * 2 + 0] = Ms;
+  ws.part_ml[slot * 128 + lane * 2 + 1] = Ls;
 }
 
 // Second pass for requests with more than one segment: left-fold the segment
-// results in ascending order (the same fold as above, element by element) and
-// write the output.  One workgroup per (KV head, request); thread t owns the
-// same 16 outputs as thread t of the first pass.
+// results in ascending order (the fold above, element by element) and write
+// the output.  One workgroup per (KV head, request); thread t takes lane
+// t % 64 of the first pass and its values 16(t/64) .. 16(t/64)+15 (one
+// 32-dim block d = t/64 of row (t%64) % 32).
 __global__ __launch_bounds__(256) void attn_combine_kernel(const int32_t* __restrict__ ctx,
                                                            uint16_t* __restrict__ out, int q_len, int Hq,
                                                            int Hkv, int max_blocks, int seg_tokens, int nseg_max,
                                                            AttnWs ws) {
   const int kvh = blockIdx.x, r = blockIdx.y;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
+  const int tid = threadIdx.x, d = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
   const int G = Hq / Hkv, nrows = q_len * G;
   const int n_tok = min(ctx[r] + q_len, max_blocks * 16);
   const int nseg = (n_tok + seg_tokens - 1) / seg_tokens;
   if (nseg <= 1 || li >= nrows) return;  // single segment: written by the first pass
   const int jq = li / G, hq = kvh * G + li % G;
+  const int64_t slot0 = ((int64_t)r * Hkv + kvh) * nseg_max;
   float M = -INFINITY, Lt = 0.0f, O[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) O[k] = 0.0f;
-  for (int s2 = 0; s2 < nseg; ++s2) {
-    const int64_t sl = ((int64_t)r * Hkv + kvh) * nseg_max + s2;
-    float o2[16];
+  // segment s + 1 is loaded while segment s is folded
+  float cur[16], nxt[16], cm, cl, nm = 0.0f, nl = 0.0f;
+  auto load = [&](int s2, float (&o)[16], float& m, float& l) {
+    const int64_t sl = slot0 + s2;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) o2[k] = __builtin_nontemporal_load(ws.part_o + sl * 4096 + tid + 256 * k);
-    const float m2 = ws.part_ml[sl * 128 + lane * 2 + 0];
-    const float l2 = ws.part_ml[sl * 128 + lane * 2 + 1];
-    fold16(M, Lt, O, m2, l2, o2);
+    for (int k = 0; k < 16; ++k) o[k] = __builtin_nontemporal_load(ws.part_o + sl * 4096 + (16 * d + k) * 64 + lane);
+    m = ws.part_ml[sl * 128 + lane * 2 + 0];
+    l = ws.part_ml[sl * 128 + lane * 2 + 1];
+  };
+  load(0, cur, cm, cl);
+  for (int s2 = 0; s2 < nseg; ++s2) {
+    if (s2 + 1 < nseg) load(s2 + 1, nxt, nm, nl);
+    fold_into<16>(M, Lt, O, cm, cl, cur);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) cur[k] = nxt[k];
+    cm = nm;
+    cl = nl;
   }
   const float inv = Lt > 0.0f ? __fdiv_rn(1.0f, Lt) : 0.0f;
-  uint16_t* orow = out + (((int64_t)r * q_len + jq) * Hq + hq) * kHD;
+  uint16_t* orow = out + (((int64_t)r * q_len + jq) * Hq + hq) * kHD + 32 * d + 4 * g;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const int v = wave + 4 * k;
-    const int vv = v & 15;
-    orow[32 * (v >> 4) + 8 * (vv >> 2) + 4 * g + (vv & 3)] = f2bf(__fmul_rn(O[k], inv));
+  for (int k4 = 0; k4 < 4; ++k4) {
+    const uint32_t w0 = (uint32_t)f2bf(__fmul_rn(O[4 * k4 + 0], inv)) | ((uint32_t)f2bf(__fmul_rn(O[4 * k4 + 1], inv)) << 16);
+    const uint32_t w1 = (uint32_t)f2bf(__fmul_rn(O[4 * k4 + 2], inv)) | ((uint32_t)f2bf(__fmul_rn(O[4 * k4 + 3], inv)) << 16);
+    *reinterpret_cast<uint2*>(orow + 8 * k4) = make_uint2(w0, w1);
   }
 }
 
@@ -480,7 +517,7 @@ static biv_status launch_attn_bf16(const char* who, const void* q, int64_t q_str
   AttnWs ws;
   ws.part_o = static_cast<float*>(workspace);
   ws.part_ml = ws.part_o + (size_t)R * Hkv * nseg_max * 4096;
-  hipLaunchKernelGGL(attn_bf16_kernel, dim3(nseg_max, Hkv, R), dim3(64 * kWaves), 0, s, static_cast<const uint16_t*>(q), q_stride,
+  hipLaunchKernelGGL(attn_bf16_kernel, dim3(nseg_max, Hkv, R), dim3(64), 0, s, static_cast<const uint16_t*>(q), q_stride,
                      static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache), block_table, ctx,
                      static_cast<uint16_t*>(out), q_len, Hq, Hkv, max_blocks, num_blocks, scale * kLog2e,
                      seg_tokens, nseg_max, ws);
