@@ -8,9 +8,11 @@ pages, then Gumbel-max verification of the candidates (the KV overwrite of the
 fast-path slots runs inside every layer).  Inputs are resident in HBM before
 the timed region.
 
-Prints ONE JSON line: verified tokens/s, the attention kernel's roofline
-(HBM-bound; bytes = one read of each visible K/V row, timed with HIP events on
-the stream it runs on), and the CPU oracle timed on a bounded sample.
+Prints ONE JSON line: verified tokens/s, the slowdown of the invariant pass
+against the same pass with split-K GEMMs and load-adaptive attention splits,
+the attention kernel's roofline (HBM-bound; bytes = one read of each visible
+K/V row, timed with HIP events on the stream it runs on), and the CPU oracle
+timed on a bounded sample.
 
     python bench.py [--steps 10] [--warmup 3] [--gpus 1] [--no-cpu-baseline]
 """
@@ -37,6 +39,11 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--layers", type=int, default=32, help=argparse.SUPPRESS)  # full model unless debugging
+    p.add_argument("--micro", action="store_true",
+                   help="instead of the pass: the per-kernel sweeps (RMSNorm+GEMM over M, attention over B, "
+                        "Gumbel verify), one JSON line each, with rooflines, split-K/adaptive slowdowns and "
+                        "oracle timings")
+    p.add_argument("--iters", type=int, default=20, help="timed calls per point in --micro")
     return p.parse_args()
 
 
@@ -94,10 +101,53 @@ def setup(torch, n_layers):
                 noise=noise)
 
 
-def cpu_baseline(torch, env, n_layers):
-    """The oracle, untouched, on a bounded sample of the same workload: one
-    decoder layer over all 512 rows plus the final norm, lm_head and verify,
-    extrapolated to the full depth as 32 * t_layer + t_head per pass."""
+class SplitVariants:
+    """The pass's GEMMs and attention swapped for their non-invariant
+    counterparts: split-K with the split count chosen from the shape
+    (gemm_splitk, auto) and attention with the KV split chosen from the load
+    (attn_decode_adaptive, auto).  Each owns its workspaces."""
+
+    def __init__(self, torch, biv, R, Hkv, max_blocks):
+        self.torch, self.biv = torch, biv
+        self.split = biv.attn_adaptive_split(R, Hkv, max_blocks)
+        self.attn_ws = torch.empty(max(biv.attn_workspace_bytes(R, Hkv, max_blocks, self.split), 16),
+                                   dtype=torch.uint8, device="cuda")
+        self.gemm_ws = {}
+        self.splits = {}
+
+    def gemm(self, a, b, c, accumulate=False):
+        M, K = a.shape
+        N = b.shape[0]
+        sp = self.biv.splitk_auto_splits(M, N, K)
+        self.splits[(N, K)] = sp
+        ws = self.gemm_ws.get((M, N, sp))
+        if ws is None:
+            ws = self.torch.empty(max(self.biv.splitk_workspace_bytes(M, N, sp), 16), dtype=self.torch.uint8,
+                                  device="cuda")
+            self.gemm_ws[(M, N, sp)] = ws
+        return self.biv.gemm_splitk(a, b, c, sp, ws, accumulate=accumulate)
+
+    def attn(self, q, k_cache, v_cache, block_table, ctx, out, q_len, scale, workspace=None):
+        return self.biv.attn_decode_adaptive(q, k_cache, v_cache, block_table, ctx, out, q_len, scale, self.attn_ws,
+                                             split_tokens=self.split)
+
+
+def time_passes(torch, model, batch, caches, steps, **kw):
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        model.verify(batch, caches, **kw)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def cpu_baseline(torch, env, n_layers, sample_layers=3):
+    """The oracle, untouched, on a bounded sample of the same workload: the
+    first `sample_layers` decoder layers over all 512 rows, then the final
+    norm, lm_head and verify; extrapolated to the full depth as
+    n_layers * mean(t_layer) + t_head per pass."""
     import oracle
     import workloads as wl
     from threadpoolctl import threadpool_info
@@ -111,41 +161,258 @@ def cpu_baseline(torch, env, n_layers):
         b = t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
         return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
-    L0 = dw["layers"][0]
-    wqkv, wgu = f64(L0["wqkv"]), f64(L0["w_gu"])
-    layer = dict(attn_norm=f64(L0["attn_norm"]), wq=wqkv[:q], wk=wqkv[q:q + kv], wv=wqkv[q + kv:], wo=f64(L0["wo"]),
-                 ffn_norm=f64(L0["ffn_norm"]), w_gate=wgu[:F], w_up=wgu[F:], w_down=f64(L0["w_down"]))
-    ow = dict(shape=wl.ModelShape(1, H, sh.heads, sh.kv_heads, D, F, sh.vocab, sh.eps, sh.rope_theta),
-              embed=f64(dw["embed"]), lm_head=None, final_norm=f64(dw["final_norm"]), layers=[layer])
     used = sorted({int(b) for b in lay.block_table[:n].ravel() if b >= 0})
     remap = {b: i for i, b in enumerate(used)}
-    kc = f64(env["caches"][0][0][used])
-    vc = f64(env["caches"][0][1][used])
     bt = np.vectorize(lambda b: remap.get(int(b), -1))(lay.block_table[:n]).astype(np.int32)
     toks = np.concatenate([env["t0"][:n, None], env["cand"][:n, :K_CAND - 1]], axis=1)
     lm = f64(dw["lm_head"])
-    # one layer (the oracle's decoder forward with a 1-layer model and a
-    # throwaway head), timed apart from the head
-    ow["lm_head"] = lm[:1]
-    t = time.perf_counter()
-    oracle.decoder_forward(ow, toks, ctx[:n], [kc], [vc], bt)
-    t_layer = time.perf_counter() - t
+    t_layers = []
+    for li in range(min(sample_layers, n_layers)):
+        Ld = dw["layers"][li]
+        wqkv, wgu = f64(Ld["wqkv"]), f64(Ld["w_gu"])
+        layer = dict(attn_norm=f64(Ld["attn_norm"]), wq=wqkv[:q], wk=wqkv[q:q + kv], wv=wqkv[q + kv:],
+                     wo=f64(Ld["wo"]), ffn_norm=f64(Ld["ffn_norm"]), w_gate=wgu[:F], w_up=wgu[F:],
+                     w_down=f64(Ld["w_down"]))
+        ow = dict(shape=wl.ModelShape(1, H, sh.heads, sh.kv_heads, D, F, sh.vocab, sh.eps, sh.rope_theta),
+                  embed=f64(dw["embed"]), lm_head=lm[:1], final_norm=f64(dw["final_norm"]), layers=[layer])
+        kc = f64(env["caches"][li][0][used])
+        vc = f64(env["caches"][li][1][used])
+        # one layer: the oracle's decoder forward with a 1-layer model and a
+        # throwaway one-row head, timed apart from the real head
+        t = time.perf_counter()
+        oracle.decoder_forward(ow, toks, ctx[:n], [kc], [vc], bt)
+        t_layers.append(time.perf_counter() - t)
+        del kc, vc, wqkv, wgu, layer
     x = wl.normal_f32(1, (n * K_CAND, H)).astype(np.float64)
     t = time.perf_counter()
-    logits = oracle.linear(oracle.rmsnorm(x, ow["final_norm"], sh.eps), lm)
+    logits = oracle.linear(oracle.rmsnorm(x, f64(dw["final_norm"]), sh.eps), lm)
     oracle.gumbel_verify(logits.astype(np.float32).reshape(n, K_CAND, -1), env["noise"][:n], env["cand"][:n])
     t_head = time.perf_counter() - t
+    t_layer = float(np.mean(t_layers))
     t_pass = n_layers * t_layer + t_head
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": round(n * K_CAND / t_pass, 3), "unit": "verified tok/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"1 of {n_layers} layers + lm_head/verify over all {n * K_CAND} rows, fp64; "
-                      f"t_layer={t_layer:.2f}s t_head={t_head:.2f}s; pass = {n_layers}*t_layer + t_head "
+            "sample": f"{len(t_layers)} of {n_layers} layers + lm_head/verify over all {n * K_CAND} rows, fp64; "
+                      f"t_layer={t_layer:.2f}s (mean) t_head={t_head:.2f}s; pass = {n_layers}*t_layer + t_head "
                       f"(extrapolated)"}
+
+
+# ---------------------------------------------------------------------------
+# --micro: the kernel-level workloads (RMSNorm+GEMM microbench, attention at
+# batch 1..256 with contexts U[512, 32768], Gumbel verify at [64, 8, 128256])
+# ---------------------------------------------------------------------------
+
+MFMA_PEAK_TFLOPS = 2500.0
+
+
+def _event_times(torch, fn, iters, warmup=5, pre=None):
+    """Median and p90 (ms) of per-call HIP event pairs on the current stream;
+    `pre` runs before each call, outside the pair."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    pairs = []
+    for i in range(iters):
+        if pre is not None:
+            pre()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn(i)
+        e.record()
+        pairs.append((s, e))
+    torch.cuda.synchronize()
+    t = np.sort([s.elapsed_time(e) for s, e in pairs])
+    return float(np.median(t)), float(t[min(len(t) - 1, int(math.ceil(0.9 * len(t))) - 1)])
+
+
+def _f64_bf16(torch, t):
+    b = t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def micro_norm_gemm(torch, biv, iters):
+    """RMSNorm over 4096 (bf16 gamma ~ N(1, 0.1)) feeding a GEMM with a bf16
+    weight [14336, 4096] ~ N(0, 0.02); M in 1..512; four weight copies rotate
+    so that the weight is read from HBM each call."""
+    import oracle
+    import workloads as wl
+
+    H, N, eps = 4096, 14336, 1e-6
+    x_all = torch.from_numpy(wl.normal_bf16(wl.SEEDS["norm_x"], (512, H)).view(np.int16)).cuda().view(torch.bfloat16)
+    gamma = torch.from_numpy(wl.normal_bf16(wl.SEEDS["norm_gamma"], (H,), std=0.1, mean=1.0).view(np.int16)).cuda()
+    gamma = gamma.view(torch.bfloat16)
+    ws = [wl._torch_normal((N, H), wl.SEEDS["gemm_w"], i, 0.02, "cuda", torch.bfloat16) for i in range(4)]
+    points = []
+    for M in [1 << i for i in range(10)]:
+        x = x_all[:M]
+        h = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+        out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        sp = biv.splitk_auto_splits(M, N, H)
+        wsk = torch.empty(max(biv.splitk_workspace_bytes(M, N, sp), 16), dtype=torch.uint8, device="cuda")
+
+        def run_bi(i):
+            biv.rmsnorm_bi(x, gamma, h, eps)
+            biv.gemm_bi(h, ws[i % 4], out)
+
+        def run_sk(i):
+            biv.rmsnorm_bi(x, gamma, h, eps)
+            biv.gemm_splitk(h, ws[i % 4], out, sp, wsk)
+
+        t_bi, p90 = _event_times(torch, run_bi, iters)
+        t_sk, _ = _event_times(torch, run_sk, iters)
+        byts = N * H * 2 + M * H * 2 * 2 + M * N * 2
+        flops = 2.0 * M * N * H
+        t_roof = max(byts / (HBM_PEAK_GBS * 1e9), flops / (MFMA_PEAK_TFLOPS * 1e12)) * 1e3
+        points.append({"M": M, "ms": round(t_bi, 5), "ms_p90": round(p90, 5),
+                       "bound": "hbm" if byts / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_PEAK_TFLOPS * 1e12) else "mfma",
+                       "roofline_ms": round(t_roof, 5), "frac": round(t_roof / t_bi, 4),
+                       "splitk_splits": sp, "splitk_ms": round(t_sk, 5), "slowdown_vs_splitk": round(t_bi / t_sk, 4)})
+        print(f"[micro] rmsnorm+gemm M={M}: {t_bi * 1e3:.1f} us (roof {t_roof * 1e3:.1f}), split-K x{sp} "
+              f"{t_sk * 1e3:.1f} us", file=sys.stderr, flush=True)
+    # oracle: the same two steps in fp64 on the host
+    w64 = _f64_bf16(torch, ws[0])
+    g64 = _f64_bf16(torch, gamma)
+    x64 = _f64_bf16(torch, x_all)
+    cpu = []
+    for M in (1, 64, 512):
+        t = time.perf_counter()
+        oracle.linear(oracle.rmsnorm(x64[:M], g64, eps), w64)
+        cpu.append({"M": M, "s": round(time.perf_counter() - t, 4)})
+    return {"workload": "rmsnorm_bi + gemm_bi: x [M,4096] bf16 ~N(0,1), gamma ~N(1,0.1), W [14336,4096] bf16 "
+                        "~N(0,0.02), bf16 out; 4 rotating weight copies",
+            "points": points, "cpu_oracle": {"kind": "oracle", "fp64": True, "threads": _threads(), "runs": cpu}}
+
+
+def micro_attention(torch, biv, iters):
+    """Decode attention, 32 Q / 8 KV heads x 128, 16-token pages placed by a
+    seeded permutation, contexts U[512, 32768]; batch B takes the first B
+    requests; q_len 1 (decode) and 8 (verify-shaped).  A 512 MiB write before
+    every timed call evicts the 256 MB last-level cache."""
+    import oracle
+    import workloads as wl
+
+    Rmax, Hq, Hkv, D = 256, 32, 8, 128
+    ctx_all = wl.context_lengths(wl.SEEDS["attn_len"], Rmax, 512, 32768)
+    lay = wl.paged_layout(ctx_all, 8, seed=wl.SEEDS["attn_perm"])
+    kc = wl._torch_normal((lay.num_blocks, Hkv, 16, D), wl.SEEDS["attn_qkv"], 1, 1.0, "cuda", torch.bfloat16)
+    vc = wl._torch_normal((lay.num_blocks, Hkv, 16, D), wl.SEEDS["attn_qkv"], 2, 1.0, "cuda", torch.bfloat16)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    bt_all = torch.from_numpy(lay.block_table).cuda()
+    cx_all = torch.from_numpy(lay.ctx).cuda()
+    scale = 1.0 / math.sqrt(D)
+    out = {}
+    for q_len in (1, 8):
+        q_all = wl._torch_normal((Rmax * q_len, Hq * D), wl.SEEDS["attn_qkv"], 10 + q_len, 1.0, "cuda",
+                                 torch.bfloat16)
+        o = torch.empty((Rmax * q_len, Hq, D), dtype=torch.bfloat16, device="cuda")
+        points = []
+        for B in [1 << i for i in range(9)]:
+            bt, cx, q = bt_all[:B].contiguous(), cx_all[:B].contiguous(), q_all[:B * q_len]
+            ob = o[:B * q_len]
+            wsb = torch.empty(biv.attn_workspace_bytes(B, Hkv, lay.max_blocks), dtype=torch.uint8, device="cuda")
+            split = biv.attn_adaptive_split(B, Hkv, lay.max_blocks)
+            wsa = torch.empty(max(biv.attn_workspace_bytes(B, Hkv, lay.max_blocks, split), 16), dtype=torch.uint8,
+                              device="cuda")
+            run_bi = lambda i: biv.attn_decode_bi(q, kc, vc, bt, cx, ob, q_len, scale, wsb)
+            run_ad = lambda i: biv.attn_decode_adaptive(q, kc, vc, bt, cx, ob, q_len, scale, wsa, split_tokens=split)
+            t_bi, p90 = _event_times(torch, run_bi, iters, pre=flush.zero_)
+            t_ad, _ = _event_times(torch, run_ad, iters, pre=flush.zero_)
+            byts = float((ctx_all[:B].astype(np.int64) + q_len).sum()) * Hkv * D * 2 * 2
+            t_roof = byts / (HBM_PEAK_GBS * 1e9) * 1e3
+            points.append({"B": B, "ms": round(t_bi, 5), "ms_p90": round(p90, 5), "bytes": byts,
+                           "GBps": round(byts / (t_bi * 1e-3) / 1e9, 1), "roofline_ms": round(t_roof, 5),
+                           "frac": round(t_roof / t_bi, 4), "adaptive_split": split, "adaptive_ms": round(t_ad, 5),
+                           "slowdown_vs_adaptive": round(t_bi / t_ad, 4)})
+            print(f"[micro] attention q_len={q_len} B={B}: {t_bi * 1e3:.1f} us ({t_roof / t_bi:.2f} of HBM), "
+                  f"adaptive split {split}: {t_ad * 1e3:.1f} us", file=sys.stderr, flush=True)
+        out[f"q_len={q_len}"] = points
+    # oracle: decode (q_len 1) at B = 1 and 16, on host copies of the pages used
+    cpu = []
+    q1 = _f64_bf16(torch, wl._torch_normal((16, Hq * D), wl.SEEDS["attn_qkv"], 11, 1.0, "cuda", torch.bfloat16))
+    for B in (1, 16):
+        used = sorted({int(b) for b in lay.block_table[:B].ravel() if b >= 0})
+        remap = {b: i for i, b in enumerate(used)}
+        idx = torch.tensor(used, device="cuda")
+        k64, v64 = _f64_bf16(torch, kc[idx]), _f64_bf16(torch, vc[idx])
+        bt64 = np.vectorize(lambda b: remap.get(int(b), -1))(lay.block_table[:B]).astype(np.int32)
+        t = time.perf_counter()
+        oracle.attention(q1[:B].reshape(B, Hq, D), k64, v64, bt64, ctx_all[:B], 1, scale)
+        cpu.append({"B": B, "q_len": 1, "s": round(time.perf_counter() - t, 4)})
+        del k64, v64
+    return {"workload": "attn_decode_bi: Q 32 heads, K/V 8 heads x 128 bf16 ~N(0,1), 16-token pages (seeded "
+                        "permutation), contexts U[512,32768], batch = first B of 256 requests; cache flushed "
+                        "before each call",
+            "points": out, "cpu_oracle": {"kind": "oracle", "fp64": True, "threads": _threads(), "runs": cpu}}
+
+
+def micro_verify(torch, biv, iters):
+    """Gumbel verify on logits [64, 8, 128256] ~ N(0, 9) fp32 with planted
+    near-ties, noise from the seeded hash, candidates with a first divergence
+    d ~ U{0..8}."""
+    import oracle
+    import workloads as wl
+
+    R, K, V = 64, 8, 128256
+    logits = wl.normal_f32(wl.SEEDS["verify_logits"], (R, K, V), std=3.0)
+    pos = np.arange(K)[None, :] + 1 + wl.context_lengths(wl.SEEDS["verify_plant"], R, 2048, 8192)[:, None]
+    noise = wl.gumbel_noise(wl.SEEDS["verify_noise"], np.repeat(np.arange(R), K).reshape(R, K), pos, V)
+    tgt, _, _ = oracle.gumbel_verify(logits, noise, np.zeros((R, K), np.int32))
+    d = wl.rng(wl.SEEDS["verify_plant"]).integers(0, K + 1, size=R)
+    cand = wl.plant_divergence(tgt, d, V, wl.SEEDS["verify_plant"])
+    t = time.perf_counter()
+    o_tgt, o_acc, o_next = oracle.gumbel_verify(logits, noise, cand)
+    t_cpu = time.perf_counter() - t
+    lg = torch.from_numpy(logits.reshape(R * K, V)).cuda()
+    nz = torch.from_numpy(noise.reshape(R * K, V)).cuda()
+    cd = torch.from_numpy(cand).cuda()
+    tg = torch.empty((R, K), dtype=torch.int32, device="cuda")
+    ac = torch.empty(R, dtype=torch.int32, device="cuda")
+    nx = torch.empty(R, dtype=torch.int32, device="cuda")
+    run = lambda i: biv.gumbel_verify(lg, nz, cd, tg, ac, nx)
+    t_gpu, p90 = _event_times(torch, run, iters)
+    exact = bool(np.array_equal(tg.cpu().numpy(), o_tgt) and np.array_equal(ac.cpu().numpy(), o_acc)
+                 and np.array_equal(nx.cpu().numpy(), o_next))
+    byts = 2.0 * R * K * V * 4
+    t_roof = byts / (HBM_PEAK_GBS * 1e9) * 1e3
+    print(f"[micro] gumbel_verify: {t_gpu * 1e3:.1f} us (roof {t_roof * 1e3:.1f}), oracle {t_cpu:.2f} s",
+          file=sys.stderr, flush=True)
+    return {"workload": "gumbel_verify: logits [64,8,128256] fp32 ~N(0,9), seeded Gumbel noise table, planted "
+                        "first divergence d ~ U{0..8}",
+            "ms": round(t_gpu, 5), "ms_p90": round(p90, 5), "roofline_ms": round(t_roof, 5),
+            "frac": round(t_roof / t_gpu, 4), "rows_per_s": round(R * K / (t_gpu * 1e-3), 1),
+            "bitwise_equal_to_oracle": exact,
+            "cpu_oracle": {"kind": "oracle", "threads": _threads(), "s": round(t_cpu, 4),
+                           "rows_per_s": round(R * K / t_cpu, 1)}}
+
+
+def _threads():
+    from threadpoolctl import threadpool_info
+
+    return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+
+
+def micro(args):
+    import torch
+
+    import invariant_verify_verifier_amd as biv
+
+    assert torch.cuda.is_available(), "bench.py --micro needs a GPU"
+    torch.cuda.set_device(0)
+    for name, fn in (("rmsnorm+gemm", micro_norm_gemm), ("attention", micro_attention),
+                     ("gumbel_verify", micro_verify)):
+        print(f"[micro] {name}", file=sys.stderr, flush=True)
+        res = fn(torch, biv, args.iters)
+        print(json.dumps({"micro": name, **res}), flush=True)
+        torch.cuda.empty_cache()
 
 
 def main():
     args = parse()
+    if args.micro and args.gpus == 1:
+        micro(args)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
               "(the verifier step shards by request with no inter-GPU traffic; see the design notes)",
@@ -181,7 +448,18 @@ def main():
     wall = time.perf_counter() - t0
     timer.on = False
     ms_step = start.elapsed_time(end) / args.steps
+    tgt_bi = batch.target.cpu().numpy().copy()
+    acc_bi = batch.accept_len.cpu().numpy().copy()
     W = N_REQ * K_CAND
+    # the same pass with split-K GEMMs and load-adaptive attention splits
+    # (not batch-invariant): slowdown = t_invariant / t_variant
+    print("[bench] split-K / adaptive-split variant pass", file=sys.stderr, flush=True)
+    var = SplitVariants(torch, biv, N_REQ, env["sh"].kv_heads, env["lay"].max_blocks)
+    model.verify(batch, caches, attn_fn=var.attn, gemm_fn=var.gemm)
+    torch.cuda.synchronize()
+    ms_var = time_passes(torch, model, batch, caches, args.steps, attn_fn=var.attn, gemm_fn=var.gemm)
+    tgt_var = batch.target.cpu().numpy()
+    acc_var = batch.accept_len.cpu().numpy()
     value = W / (ms_step / 1e3)
     sh = env["sh"]
     attn_bytes = float(np.sum(ctx.astype(np.int64) + K_CAND)) * sh.kv_heads * sh.head_dim * 2 * 2
@@ -205,7 +483,13 @@ def main():
                                "16-token pages, Gumbel verify + KV overwrite",
                    "N": N_REQ, "K": K_CAND, "W": W, "ctx_mean": float(ctx.mean()),
                    "wall_s_timed": round(wall, 3)},
-        "roofline": {"kernel": "attn_bf16_kernel (attn_decode_bi)", "bound": "hbm",
+        "slowdown_vs_splitk": {"value": round(ms_step / ms_var, 4), "ms_variant": round(ms_var, 4),
+                               "variant": "gemm_splitk (auto splits per shape: "
+                                          + ", ".join(f"N={n},K={k}:{sp}" for (n, k), sp in sorted(var.splits.items()))
+                                          + f") + attn_decode_adaptive (split {var.split} tokens)",
+                               "target_rows_differing": int((tgt_var != tgt_bi).sum()),
+                               "accept_len_differing": int((acc_var != acc_bi).sum())},
+        "roofline": {"kernel": "attn_decode_bi (attn_bf16_kernel + attn_combine_kernel)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "bytes_per_launch": attn_bytes, "avg_launch_ms": round(attn_ms, 5),

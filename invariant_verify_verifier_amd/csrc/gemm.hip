@@ -249,17 +249,42 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_kernel(const 
     if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
     const unsigned char* As = smem + (kt % STAGES) * STAGE;
     const unsigned char* Bs = As + A_BYTES;
+    // Fragments are read ahead of the MFMAs that use them, so that LDS
+    // latency overlaps matrix work (with one wave per SIMD nothing else
+    // hides it).  Small wave tiles read the whole stage up front; large ones
+    // read step ks + 1 while step ks multiplies.  The sched_barrier keeps the
+    // compiler from sinking the reads back next to their uses.
+    constexpr int KS = kDBK / 16;
+    constexpr bool kWhole = (FM + FN) <= 3;
+    constexpr int NBUF = kWhole ? KS : 2;
+    bf16x8 a[NBUF][FM], b[NBUF][FN];
+    auto read = [&](int ks, int buf) {
 #pragma unroll
-    for (int ks = 0; ks < kDBK / 16; ++ks) {
-      bf16x8 a[FM], b[FN];
+      for (int i = 0; i < FM; ++i)
+        a[buf][i] = *reinterpret_cast<const bf16x8*>(As + (wm * WM + 32 * i) * ROW + off[ks]);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) a[i] = *reinterpret_cast<const bf16x8*>(As + (wm * WM + 32 * i) * ROW + off[ks]);
+      for (int j = 0; j < FN; ++j)
+        b[buf][j] = *reinterpret_cast<const bf16x8*>(Bs + (wn * WN + 32 * j) * ROW + off[ks]);
+    };
+    if constexpr (kWhole) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) b[j] = *reinterpret_cast<const bf16x8*>(Bs + (wn * WN + 32 * j) * ROW + off[ks]);
+      for (int ks = 0; ks < KS; ++ks) read(ks, ks);
+    } else {
+      read(0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int buf = kWhole ? ks : (ks & 1);
+      if constexpr (!kWhole) {
+        if (ks + 1 < KS) read(ks + 1, (ks + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[buf][i], b[buf][j], acc[i][j], 0, 0, 0);
     }
   }
 
@@ -370,6 +395,9 @@ enum DmaTile { kTileL = 0, kTileS = 1, kTileT = 2 };
 #ifndef BIV_GEMM_L_TILE
 #define BIV_GEMM_L_TILE 256, 256, 2, 2, 4  // BM, BN, stages, waves along M, waves along N
 #endif
+#ifndef BIV_GEMM_T_TILE
+#define BIV_GEMM_T_TILE 64, 128, 3, 2, 2
+#endif
 static DmaTile dma_tile_for(int64_t N) {
   if (N >= 16384) return kTileL;  // 256 x 256, 8 waves of 128 x 64, 2 stages (128 KiB LDS)
   if (N >= 8192) return kTileS;   // 128 x 128, 2 stages (64 KiB, two per CU)
@@ -394,7 +422,7 @@ static void launch_dma(DmaTile t, const void* A, const void* B, void* C, float* 
   else if (t == kTileS)
     launch_dma_t<128, 128, 2, 2, 2, OUT_DT, EPI, kSplit>(A, B, C, partial, M, N, K, splits, k_per_split, s);
   else
-    launch_dma_t<64, 128, 3, 2, 2, OUT_DT, EPI, kSplit>(A, B, C, partial, M, N, K, splits, k_per_split, s);
+    launch_dma_t<BIV_GEMM_T_TILE, OUT_DT, EPI, kSplit>(A, B, C, partial, M, N, K, splits, k_per_split, s);
 }
 
 static biv_status check_gemm_args(const char* who, const void* A, const void* B, void* C, int64_t M, int64_t N,
