@@ -390,18 +390,29 @@ static void launch_bf16(const void* A, const void* B, void* C, float* partial, i
                      tilesM, tilesN, k_per_split);
 }
 
-// Tile of the staged kernel for a weight with N outputs (never depends on M).
-enum DmaTile { kTileL = 0, kTileS = 1, kTileT = 2 };
+// Tile of the staged kernel for a weight with N outputs: one tiling per
+// weight shape, the same for every M.  (Each output's reduction order is the
+// same under every tile -- one MFMA shape, ascending k -- so the tile only
+// decides which workgroup computes which outputs.)  Chosen by measurement at
+// M = 512 on the decoder's weights.
+enum DmaTile { kTileL = 0, kTileS = 1, kTileQ = 2, kTileT = 3 };
 #ifndef BIV_GEMM_L_TILE
 #define BIV_GEMM_L_TILE 256, 256, 2, 2, 4  // BM, BN, stages, waves along M, waves along N
 #endif
+#ifndef BIV_GEMM_S_TILE
+#define BIV_GEMM_S_TILE 128, 128, 2, 2, 4
+#endif
+#ifndef BIV_GEMM_Q_TILE
+#define BIV_GEMM_Q_TILE 64, 128, 3, 2, 4
+#endif
 #ifndef BIV_GEMM_T_TILE
-#define BIV_GEMM_T_TILE 64, 128, 3, 2, 2
+#define BIV_GEMM_T_TILE 128, 64, 4, 4, 2
 #endif
 static DmaTile dma_tile_for(int64_t N) {
   if (N >= 16384) return kTileL;  // 256 x 256, 8 waves of 128 x 64, 2 stages (128 KiB LDS)
-  if (N >= 8192) return kTileS;   // 128 x 128, 2 stages (64 KiB, two per CU)
-  return kTileT;                  // 64 x 128, 3 stages (72 KiB, two per CU)
+  if (N >= 8192) return kTileS;   // 128 x 128, 8 waves of 64 x 32, 2 stages (64 KiB)
+  if (N > 4096) return kTileQ;    // 64 x 128, 8 waves of 32 x 32, 3 stages (72 KiB)
+  return kTileT;                  // 128 x 64, 8 waves of 32 x 32, 4 stages (96 KiB)
 }
 
 template <int BM, int BN, int STAGES, int WAVES_M, int WAVES_N, int OUT_DT, int EPI, bool kSplit>
@@ -420,7 +431,9 @@ static void launch_dma(DmaTile t, const void* A, const void* B, void* C, float* 
   if (t == kTileL)
     launch_dma_t<BIV_GEMM_L_TILE, OUT_DT, EPI, kSplit>(A, B, C, partial, M, N, K, splits, k_per_split, s);
   else if (t == kTileS)
-    launch_dma_t<128, 128, 2, 2, 2, OUT_DT, EPI, kSplit>(A, B, C, partial, M, N, K, splits, k_per_split, s);
+    launch_dma_t<BIV_GEMM_S_TILE, OUT_DT, EPI, kSplit>(A, B, C, partial, M, N, K, splits, k_per_split, s);
+  else if (t == kTileQ)
+    launch_dma_t<BIV_GEMM_Q_TILE, OUT_DT, EPI, kSplit>(A, B, C, partial, M, N, K, splits, k_per_split, s);
   else
     launch_dma_t<BIV_GEMM_T_TILE, OUT_DT, EPI, kSplit>(A, B, C, partial, M, N, K, splits, k_per_split, s);
 }
