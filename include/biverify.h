@@ -102,7 +102,13 @@ biv_status rmsnorm_bi(const void* x, biv_dtype x_dt, const void* gamma, void* y,
  *   in_dt BIV_F32: fp32 FMA chain over k ascending.
  * The rounding of C is once, from fp32.  M >= 0, N >= 1, K >= 1.
  * ------------------------------------------------------------------------ */
-enum { BIV_EPI_STORE = 0, BIV_EPI_ACCUM = 1 };
+enum { BIV_EPI_STORE = 0, BIV_EPI_ACCUM = 1, BIV_EPI_SWIGLU = 2 };
+/* epilogue BIV_EPI_SWIGLU (SwiGLU feed-forward, gate and up projections in one
+ * product): B holds the gate and up weights interleaved in blocks of 32 rows
+ * (rows 64b .. 64b+31 are gate rows 32b .. 32b+31, rows 64b+32 .. 64b+63 the
+ * up rows 32b .. 32b+31); C is [M, N/2] and C[m, j] = silu(g) * u with g, u the
+ * fp32 results of gate and up row j, silu(g) = g / (1 + exp(-g)), rounded once.
+ * bf16 inputs only, N % 64 == 0 and K % 64 == 0. */
 
 biv_status gemm_bi(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                    biv_dtype in_dt, biv_dtype out_dt, int epilogue, biv_stream stream);
@@ -215,9 +221,13 @@ biv_status biv_rope_table(float* cos_sin, int max_pos, int D, double theta);
 biv_status rope_apply(void* x, int64_t stride, const int32_t* pos, const float* cos_sin, int T,
                       int n_heads, int D, int max_pos, biv_dtype dt, biv_stream stream);
 
-/* out[m, n] = silu(gu[m, n]) * gu[m, N + n], silu(g) = g / (1 + exp(-g)),
- * fp32 math; gu [M, 2N], out [M, N], both in dt. */
-biv_status swiglu(const void* gu, void* out, int64_t M, int64_t N, biv_dtype dt, biv_stream stream);
+/* out[m, n] = silu(g) * u, silu(g) = g / (1 + exp(-g)), fp32 math; gu [M, 2N],
+ * out [M, N], both in dt.  block == 0: g = gu[m, n], u = gu[m, N + n] (gate
+ * and up halves); block > 0 (dividing N): the columns come in groups of
+ * 2*block, gate block then up block, as in the BIV_EPI_SWIGLU weight layout
+ * (block 32): g = gu[m, 2*block*(n/block) + n%block], u = that + block. */
+biv_status swiglu(const void* gu, void* out, int64_t M, int64_t N, int64_t block, biv_dtype dt,
+                  biv_stream stream);
 
 /* --------------------------------------------------------------------------
  * Non-invariant comparison variants (same contracts as above, NOT batch

@@ -6,6 +6,7 @@ that sequences those kernels (verifier).  There is no CPU or PyTorch
 fallback: importing fails if the library has not been built.
 """
 from ._lib import (  # noqa: F401
+    SWIGLU_BLOCK,
     BivError,
     abi_version,
     attn_adaptive_split,
@@ -18,6 +19,7 @@ from ._lib import (  # noqa: F401
     gemm_splitk,
     gumbel_verify,
     kv_overwrite,
+    pack_gate_up,
     rmsnorm_bi,
     rope_apply,
     rope_table,

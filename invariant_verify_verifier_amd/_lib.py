@@ -25,7 +25,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 BIV_OK, BIV_EINVAL, BIV_EUNSUPPORTED, BIV_EHIP = 0, 1, 2, 3
 BIV_F32, BIV_BF16 = 0, 1
-BIV_EPI_STORE, BIV_EPI_ACCUM = 0, 1
+BIV_EPI_STORE, BIV_EPI_ACCUM, BIV_EPI_SWIGLU = 0, 1, 2
 ATTN_CHUNK_TOKENS = 256
 ATTN_SEG_TOKENS = 1024
 
@@ -45,7 +45,7 @@ _SIGS = {
     "embed_rows": ([_vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp], _i32),
     "biv_rope_table": ([_vp, _i32, _i32, _f64], _i32),
     "rope_apply": ([_vp, _i64, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp], _i32),
-    "swiglu": ([_vp, _vp, _i64, _i64, _i32, _vp], _i32),
+    "swiglu": ([_vp, _vp, _i64, _i64, _i64, _i32, _vp], _i32),
     "biv_splitk_workspace_bytes": ([_i64, _i64, _i32], _sz),
     "biv_splitk_auto_splits": ([_i64, _i64, _i64], _i32),
     "gemm_splitk": ([_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp, _sz, _vp], _i32),
@@ -126,16 +126,31 @@ def rmsnorm_bi(x, gamma, y, eps):
     return y
 
 
-def gemm_bi(a, b, c, accumulate=False):
-    """c[M,N] (=|+=) a[M,K] @ b[N,K]^T."""
+def gemm_bi(a, b, c, accumulate=False, swiglu=False):
+    """c[M,N] (=|+=) a[M,K] @ b[N,K]^T; with swiglu, b is the 32-row-block
+    interleaved gate/up weight (pack_gate_up) and c[M, N/2] = silu(gate) * up."""
     _contig(a, b, c)
     M, K = a.shape
     N = b.shape[0]
-    assert b.shape[1] == K and tuple(c.shape) == (M, N)
+    assert b.shape[1] == K
+    assert tuple(c.shape) == ((M, N // 2) if swiglu else (M, N))
+    assert not (swiglu and accumulate)
     _same_dtype(a, b)
-    epi = BIV_EPI_ACCUM if accumulate else BIV_EPI_STORE
+    epi = BIV_EPI_SWIGLU if swiglu else (BIV_EPI_ACCUM if accumulate else BIV_EPI_STORE)
     _check("gemm_bi", _lib.gemm_bi(_p(a), _p(b), _p(c), M, N, K, _dt(a), _dt(c), epi, _stream()))
     return c
+
+
+SWIGLU_BLOCK = 32
+
+
+def pack_gate_up(w_gate_up):
+    """[W_gate; W_up] ([2F, H]) -> the BIV_EPI_SWIGLU layout: blocks of 32 gate
+    rows followed by the 32 matching up rows (a copy; layout only)."""
+    F2, H = w_gate_up.shape
+    F = F2 // 2
+    assert F2 == 2 * F and F % SWIGLU_BLOCK == 0
+    return w_gate_up.view(2, F // SWIGLU_BLOCK, SWIGLU_BLOCK, H).transpose(0, 1).contiguous().view(F2, H)
 
 
 def attn_workspace_bytes(R, Hkv, max_blocks, seg_tokens=ATTN_SEG_TOKENS):
@@ -249,12 +264,14 @@ def rope_apply(x, pos, cos_sin, n_heads, D):
                                          cos_sin.shape[0], _dt(x), _stream()))
 
 
-def swiglu(gu, out):
+def swiglu(gu, out, block=0):
+    """out = silu(gate) * up; gate/up are the row halves of gu (block 0) or its
+    interleaved blocks (block = SWIGLU_BLOCK for the packed gate/up weight)."""
     _contig(gu, out)
     _same_dtype(gu, out)
     M, N2 = gu.shape
     assert tuple(out.shape) == (M, N2 // 2)
-    _check("swiglu", _lib.swiglu(_p(gu), _p(out), M, N2 // 2, _dt(gu), _stream()))
+    _check("swiglu", _lib.swiglu(_p(gu), _p(out), M, N2 // 2, block, _dt(gu), _stream()))
     return out
 
 

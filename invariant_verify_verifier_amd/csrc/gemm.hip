@@ -294,6 +294,25 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_kernel(const 
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int n = n0 + wn * WN + 32 * j + li;
+      if constexpr (EPI == BIV_EPI_SWIGLU) {
+        // fragment pair (j, j + 1) = gate and up blocks of the same 32
+        // outputs: packed columns 64b .. 64b+63 -> outputs 32b .. 32b+31
+        static_assert(FN % 2 == 0 && !kSplit, "SwiGLU pairs the wave's gate and up fragments");
+        if (j & 1) continue;
+        const int nc = n0 + wn * WN + 32 * j;  // a multiple of 64
+        if (nc >= N) continue;
+        const int col = (nc >> 1) + li;
+        const int64_t n_out = N >> 1;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = m0 + wm * WM + 32 * i + 8 * (v >> 2) + 4 * g + (v & 3);
+          if (m >= M) continue;
+          const float gt = acc[i][j][v], up = acc[i][j + 1][v];
+          const float act = __fdiv_rn(gt, __fadd_rn(1.0f, expf(-gt)));
+          store_from_f32(C, (int64_t)m * n_out + col, __fmul_rn(act, up), OUT_DT);
+        }
+        continue;
+      }
       if (n >= N) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -441,7 +460,8 @@ static void launch_dma(DmaTile t, const void* A, const void* B, void* C, float* 
 static biv_status check_gemm_args(const char* who, const void* A, const void* B, void* C, int64_t M, int64_t N,
                                   int64_t K, int out_dt, int epilogue) {
   BIV_REQUIRE(valid_dt(out_dt), "%s: bad out dtype %d", who, out_dt);
-  BIV_REQUIRE(epilogue == BIV_EPI_STORE || epilogue == BIV_EPI_ACCUM, "%s: bad epilogue %d", who, epilogue);
+  BIV_REQUIRE(epilogue == BIV_EPI_STORE || epilogue == BIV_EPI_ACCUM || epilogue == BIV_EPI_SWIGLU,
+              "%s: bad epilogue %d", who, epilogue);
   BIV_REQUIRE(M >= 0 && N >= 1 && K >= 1, "%s: bad sizes M=%lld N=%lld K=%lld", who, (long long)M, (long long)N,
               (long long)K);
   BIV_REQUIRE(M <= (1 << 30) && N <= (1 << 30) && K <= (1 << 30), "%s: size too large", who);
@@ -460,6 +480,20 @@ extern "C" biv_status gemm_bi(const void* A, const void* B, void* C, int64_t M, 
   if (M == 0) return BIV_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int m = (int)M, n = (int)N, k = (int)K;
+  if (epilogue == BIV_EPI_SWIGLU) {
+    BIV_REQUIRE(in_dt == BIV_BF16, "gemm_bi: the SwiGLU epilogue needs bf16 inputs");
+    BIV_REQUIRE(N % 64 == 0 && K % kDBK == 0, "gemm_bi: the SwiGLU epilogue needs N %% 64 == 0 and K %% 64 == 0 "
+                "(N=%lld K=%lld)", (long long)N, (long long)K);
+    BIV_REQUIRE(aligned16(A) && aligned16(B), "gemm_bi: bf16 path needs 16-byte aligned A and B");
+    BIV_REQUIRE((int64_t)K * 2 * 16 <= 0x7fffffff, "gemm_bi: K too large");
+    // the wide tile for every N: its waves hold two 32-column fragments, a
+    // gate block and the matching up block
+    if (out_dt == BIV_BF16)
+      launch_dma_t<BIV_GEMM_L_TILE, BIV_BF16, BIV_EPI_SWIGLU, false>(A, B, C, nullptr, m, n, k, 1, k, s);
+    else
+      launch_dma_t<BIV_GEMM_L_TILE, BIV_F32, BIV_EPI_SWIGLU, false>(A, B, C, nullptr, m, n, k, 1, k, s);
+    return launched("gemm_bi/bf16-swiglu");
+  }
   if (in_dt == BIV_BF16) {
     BIV_REQUIRE(K % 8 == 0, "gemm_bi: bf16 path needs K %% 8 == 0 (K=%lld)", (long long)K);
     BIV_REQUIRE(aligned16(A) && aligned16(B), "gemm_bi: bf16 path needs 16-byte aligned A and B");
@@ -529,6 +563,7 @@ extern "C" biv_status gemm_splitk(const void* A, const void* B, void* C, int64_t
   using namespace biv;
   biv_status st = check_gemm_args("gemm_splitk", A, B, C, M, N, K, out_dt, epilogue);
   if (st != BIV_OK) return st;
+  BIV_REQUIRE(epilogue != BIV_EPI_SWIGLU, "gemm_splitk: no SwiGLU epilogue (use swiglu() on the packed product)");
   BIV_REQUIRE(splits >= 0 && splits <= 64, "gemm_splitk: splits must be in [0, 64]");
   if (M == 0) return BIV_OK;
   BIV_REQUIRE(K % 8 == 0 && aligned16(A) && aligned16(B), "gemm_splitk: needs K %% 8 == 0 and aligned A, B");

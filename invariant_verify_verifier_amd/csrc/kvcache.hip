@@ -84,12 +84,17 @@ __global__ void rope_apply_kernel(void* __restrict__ x, int64_t stride, const in
   store_from_f32(x, ib, rb, dt);
 }
 
-__global__ void swiglu_kernel(const void* __restrict__ gu, void* __restrict__ out, int64_t M, int64_t N, int dt) {
+__global__ void swiglu_kernel(const void* __restrict__ gu, void* __restrict__ out, int64_t M, int64_t N, int64_t block,
+                              int dt) {
   const int64_t total = M * N;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
     const int64_t m = e / N, n = e - m * N;
-    const float g = load_as_f32(gu, m * 2 * N + n, dt);
-    const float u = load_as_f32(gu, m * 2 * N + N + n, dt);
+    // gate and up of output n: the two halves of the row, or the two halves
+    // of its 2*block-column group
+    const int64_t gi = block == 0 ? m * 2 * N + n : m * 2 * N + (n / block) * 2 * block + n % block;
+    const int64_t ui = block == 0 ? gi + N : gi + block;
+    const float g = load_as_f32(gu, gi, dt);
+    const float u = load_as_f32(gu, ui, dt);
     const float act = __fdiv_rn(g, __fadd_rn(1.0f, expf(-g)));
     store_from_f32(out, e, __fmul_rn(act, u), dt);
   }
@@ -158,15 +163,18 @@ extern "C" biv_status rope_apply(void* x, int64_t stride, const int32_t* pos, co
   return launched("rope_apply");
 }
 
-extern "C" biv_status swiglu(const void* gu, void* out, int64_t M, int64_t N, biv_dtype dt, biv_stream stream) {
+extern "C" biv_status swiglu(const void* gu, void* out, int64_t M, int64_t N, int64_t block, biv_dtype dt,
+                              biv_stream stream) {
   using namespace biv;
   BIV_REQUIRE(valid_dt(dt), "swiglu: bad dtype");
   BIV_REQUIRE(M >= 0 && N >= 1, "swiglu: bad sizes");
+  BIV_REQUIRE(block == 0 || (block >= 1 && N % block == 0), "swiglu: block %lld must be 0 or divide N=%lld",
+              (long long)block, (long long)N);
   if (M == 0) return BIV_OK;
   BIV_REQUIRE(gu && out, "swiglu: NULL pointer");
   const int64_t n = M * N;
   const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(n, 256), 8192);
   hipLaunchKernelGGL(swiglu_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), gu, out, M, N,
-                     (int)dt);
+                     block, (int)dt);
   return launched("swiglu");
 }

@@ -64,14 +64,19 @@ class VerifierModel:
 
     Weight layout [out_features, in_features]; Q, K, V projections fused into
     one [Hq*D + 2*Hkv*D, H] matrix and gate/up into one [2F, H] matrix, so one
-    GEMM produces each.  The residual stream is fp32; GEMM inputs are the
-    model dtype (bf16: MFMA; fp32: FMA path).
+    GEMM produces each (gate/up interleaved in 32-row blocks, so that the bf16
+    GEMM applies SwiGLU in its epilogue).  The residual stream is fp32; GEMM
+    inputs are the model dtype (bf16: MFMA; fp32: FMA path).
     """
 
     def __init__(self, shape: Shape, dtype: torch.dtype, layers, embed, lm_head, final_norm, max_pos=65536,
                  device="cuda"):
         self.shape, self.dtype, self.device = shape, dtype, device
-        self.layers, self.embed, self.lm_head, self.final_norm = layers, embed, lm_head, final_norm
+        # the model's own layer dicts: gate/up weights repacked once into the
+        # interleaved layout of the SwiGLU epilogue (the caller's tensors are
+        # left as they are)
+        self.layers = [dict(lw, w_gu=L.pack_gate_up(lw["w_gu"])) for lw in layers]
+        self.embed, self.lm_head, self.final_norm = embed, lm_head, final_norm
         self.max_pos = max_pos
         self.rope = L.rope_table(max_pos, shape.head_dim, shape.rope_theta).to(device)
         self._bufs = {}
@@ -160,8 +165,11 @@ class VerifierModel:
             attend(qkv[:, :qc], k_cache, v_cache, block_table, ctx, attn, q_len, scale, ws)
             gemm(attn.view(W, qc), lw["wo"], x, accumulate=True)
             L.rmsnorm_bi(x, lw["ffn_norm"], h, sh.eps)
-            gemm(h, lw["w_gu"], gu)
-            L.swiglu(gu, act)
+            if gemm_fn is None and self.dtype == torch.bfloat16:
+                L.gemm_bi(h, lw["w_gu"], act, swiglu=True)
+            else:
+                gemm(h, lw["w_gu"], gu)
+                L.swiglu(gu, act, block=L.SWIGLU_BLOCK)
             gemm(act, lw["w_down"], x, accumulate=True)
         L.rmsnorm_bi(x, self.final_norm, h, sh.eps)
         gemm(h, self.lm_head, logits)

@@ -52,6 +52,12 @@ def test_host_side_argument_errors(lib):
     assert b"NULL" in lib.biv_last_error()
     assert lib.gemm_bi(None, None, None, 4, 8, 8, 7, 1, 0, None) == 1  # bad dtype
     assert lib.gemm_bi(None, None, None, 0, 8, 8, 1, 1, 0, None) == 0  # M = 0: nothing to do
+    buf = ctypes.create_string_buffer(4096)
+    bp = ctypes.cast(buf, vp)
+    assert lib.gemm_bi(bp, bp, bp, 4, 128, 96, 1, 1, 2, None) == 1  # SwiGLU epilogue: K % 64 != 0
+    assert lib.gemm_bi(bp, bp, bp, 4, 96, 64, 1, 1, 2, None) == 1  # SwiGLU epilogue: N % 64 != 0
+    assert lib.gemm_bi(bp, bp, bp, 4, 128, 64, 0, 0, 2, None) == 1  # SwiGLU epilogue: fp32 inputs
+    assert lib.gemm_bi(bp, bp, bp, 4, 128, 64, 1, 1, 3, None) == 1  # unknown epilogue
     lib.rmsnorm_bi.argtypes = [vp, i32, vp, vp, i32, i64, i64, f32, vp]
     assert lib.rmsnorm_bi(None, 0, None, None, 0, 3, 0, 1e-6, None) == 1
     lib.gumbel_verify.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, vp, vp]

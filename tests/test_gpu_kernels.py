@@ -279,6 +279,61 @@ def test_gemm_bf16_cfg1_parity_and_invariance(biv):
     assert np.array_equal(bits(cp), full[perm])
 
 
+def _swiglu_ref(a_np, wg_np, wu_np):
+    a = oracle.as_f64(a_np, "bf16")
+    return oracle.silu(oracle.linear(a, oracle.as_f64(wg_np, "bf16"))) * oracle.linear(a, oracle.as_f64(wu_np, "bf16"))
+
+
+def test_gemm_swiglu_epilogue_parity_and_invariance(biv):
+    """gate/up in one product with SwiGLU applied to the fp32 results:
+    silu(A Wg^T) * (A Wu^T) against the fp64 oracle (bf16 and fp32 outputs),
+    and every row's bits identical for M = 1 .. 512."""
+    M, F, K = 512, 2048, 4096
+    a_np = wl.normal_bf16(60, (M, K))
+    wg_np = wl.normal_bf16(61, (F, K), std=0.02)
+    wu_np = wl.normal_bf16(62, (F, K), std=0.02)
+    a = dev_bf16(a_np)
+    w = biv.pack_gate_up(dev_bf16(np.concatenate([wg_np, wu_np], axis=0)))
+    announce("gemm swiglu epilogue", M, F, K)
+    c = torch.empty((M, F), dtype=torch.bfloat16, device=DEV)
+    biv.gemm_bi(a, w, c, swiglu=True)
+    cf = torch.empty((M, F), dtype=torch.float32, device=DEV)
+    biv.gemm_bi(a, w, cf, swiglu=True)
+    sync()
+    ref = _swiglu_ref(a_np, wg_np, wu_np)
+    check_bf16(f64(c), ref, "swiglu epilogue bf16")
+    check_f32(f64(cf), ref, axis=1, what="swiglu epilogue fp32")
+    full = bits(c)
+    for m in M_SWEEP:
+        cm = torch.empty((m, F), dtype=torch.bfloat16, device=DEV)
+        biv.gemm_bi(a[:m].contiguous(), w, cm, swiglu=True)
+        sync()
+        assert np.array_equal(bits(cm), full[:m]), f"rows changed at M={m}"
+
+
+def test_gemm_swiglu_epilogue_ragged_and_unfused_layout(biv):
+    """A ragged shape (M and F not multiples of the tile) against the oracle,
+    and the unfused route over the same packed weight (GEMM, then swiglu with
+    block 32) within the same tolerance."""
+    M, F, K = 77, 96, 320
+    a_np = wl.normal_bf16(63, (M, K))
+    wg_np = wl.normal_bf16(64, (F, K), std=0.05)
+    wu_np = wl.normal_bf16(65, (F, K), std=0.05)
+    a = dev_bf16(a_np)
+    w = biv.pack_gate_up(dev_bf16(np.concatenate([wg_np, wu_np], axis=0)))
+    announce("gemm swiglu ragged", M, F, K)
+    c = torch.empty((M, F), dtype=torch.float32, device=DEV)
+    biv.gemm_bi(a, w, c, swiglu=True)
+    gu = torch.empty((M, 2 * F), dtype=torch.float32, device=DEV)
+    biv.gemm_bi(a, w, gu)
+    c2 = torch.empty((M, F), dtype=torch.float32, device=DEV)
+    biv.swiglu(gu, c2, block=biv.SWIGLU_BLOCK)
+    sync()
+    ref = _swiglu_ref(a_np, wg_np, wu_np)
+    check_f32(f64(c), ref, axis=1, what="swiglu ragged")
+    check_f32(f64(c2), ref, axis=1, what="swiglu unfused over the packed weight")
+
+
 @pytest.mark.parametrize("M,N,K", [(77, 200, 264), (1, 130, 8), (129, 257, 1000), (300, 128, 4096)])
 def test_gemm_bf16_ragged_shapes(biv, M, N, K):
     a_np = wl.normal_bf16(20 + M, (M, K))
@@ -500,6 +555,13 @@ def test_rope_swiglu_embed(biv, dtype):
     sync()
     gu = oracle.as_f64(gu_np, dtype)
     chk(f64(out), oracle.silu(gu[:, :300]) * gu[:, 300:], "swiglu")
+    # interleaved layout: groups of 2*30 columns, gate 30 then up 30
+    outb = torch.empty((33, 300), dtype=x.dtype, device=DEV)
+    biv.swiglu(dev(gu_np), outb, block=30)
+    sync()
+    n = np.arange(300)
+    gi = 60 * (n // 30) + n % 30
+    chk(f64(outb), oracle.silu(gu[:, gi]) * gu[:, gi + 30], "swiglu block 30")
     tab_np = mk(112, (50, 64))
     ids = np.array([3, 49, 0, 7, -1, 50], np.int32)
     emb = torch.empty((6, 64), dtype=torch.float32, device=DEV)
