@@ -362,50 +362,46 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
 
 // Second pass for requests with more than one segment: left-fold the segment
 // results in ascending order (the fold above, element by element) and write
-// the output.  One workgroup per (KV head, request); thread t takes lane
-// t % 64 of the first pass and its values 16(t/64) .. 16(t/64)+15 (one
-// 32-dim block d = t/64 of row (t%64) % 32).
-__global__ __launch_bounds__(256) void attn_combine_kernel(const int32_t* __restrict__ ctx,
-                                                           uint16_t* __restrict__ out, int q_len, int Hq,
-                                                           int Hkv, int max_blocks, int seg_tokens, int nseg_max,
-                                                           AttnWs ws) {
+// the output.  One workgroup of 1024 threads per (KV head, request); thread t
+// takes lane t % 64 of the first pass and its values 4q .. 4q+3, q = t / 64
+// (dims 32(q/4) + 8(q%4) + 4g .. +3 of row (t%64) % 32).  Up to kCombBatch
+// segments are loaded at once, then folded in order.
+constexpr int kCombThreads = 1024, kCombBatch = 8;
+
+__global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(const int32_t* __restrict__ ctx,
+                                                                    uint16_t* __restrict__ out, int q_len, int Hq,
+                                                                    int Hkv, int max_blocks, int seg_tokens,
+                                                                    int nseg_max, AttnWs ws) {
   const int kvh = blockIdx.x, r = blockIdx.y;
-  const int tid = threadIdx.x, d = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
+  const int tid = threadIdx.x, q = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
   const int G = Hq / Hkv, nrows = q_len * G;
   const int n_tok = min(ctx[r] + q_len, max_blocks * 16);
   const int nseg = (n_tok + seg_tokens - 1) / seg_tokens;
   if (nseg <= 1 || li >= nrows) return;  // single segment: written by the first pass
   const int jq = li / G, hq = kvh * G + li % G;
   const int64_t slot0 = ((int64_t)r * Hkv + kvh) * nseg_max;
-  float M = -INFINITY, Lt = 0.0f, O[16];
+  float M = -INFINITY, Lt = 0.0f, O[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s0 = 0; s0 < nseg; s0 += kCombBatch) {
+    float o[kCombBatch][4], m[kCombBatch], l[kCombBatch];
 #pragma unroll
-  for (int k = 0; k < 16; ++k) O[k] = 0.0f;
-  // segment s + 1 is loaded while segment s is folded
-  float cur[16], nxt[16], cm, cl, nm = 0.0f, nl = 0.0f;
-  auto load = [&](int s2, float (&o)[16], float& m, float& l) {
-    const int64_t sl = slot0 + s2;
+    for (int b = 0; b < kCombBatch; ++b) {
+      if (s0 + b < nseg) {
+        const int64_t sl = slot0 + s0 + b;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) o[k] = __builtin_nontemporal_load(ws.part_o + sl * 4096 + (16 * d + k) * 64 + lane);
-    m = ws.part_ml[sl * 128 + lane * 2 + 0];
-    l = ws.part_ml[sl * 128 + lane * 2 + 1];
-  };
-  load(0, cur, cm, cl);
-  for (int s2 = 0; s2 < nseg; ++s2) {
-    if (s2 + 1 < nseg) load(s2 + 1, nxt, nm, nl);
-    fold_into<16>(M, Lt, O, cm, cl, cur);
+        for (int c = 0; c < 4; ++c) o[b][c] = __builtin_nontemporal_load(ws.part_o + sl * 4096 + (4 * q + c) * 64 + lane);
+        m[b] = ws.part_ml[sl * 128 + lane * 2 + 0];
+        l[b] = ws.part_ml[sl * 128 + lane * 2 + 1];
+      }
+    }
 #pragma unroll
-    for (int k = 0; k < 16; ++k) cur[k] = nxt[k];
-    cm = nm;
-    cl = nl;
+    for (int b = 0; b < kCombBatch; ++b)
+      if (s0 + b < nseg) fold_into<4>(M, Lt, O, m[b], l[b], o[b]);
   }
   const float inv = Lt > 0.0f ? __fdiv_rn(1.0f, Lt) : 0.0f;
-  uint16_t* orow = out + (((int64_t)r * q_len + jq) * Hq + hq) * kHD + 32 * d + 4 * g;
-#pragma unroll
-  for (int k4 = 0; k4 < 4; ++k4) {
-    const uint32_t w0 = (uint32_t)f2bf(__fmul_rn(O[4 * k4 + 0], inv)) | ((uint32_t)f2bf(__fmul_rn(O[4 * k4 + 1], inv)) << 16);
-    const uint32_t w1 = (uint32_t)f2bf(__fmul_rn(O[4 * k4 + 2], inv)) | ((uint32_t)f2bf(__fmul_rn(O[4 * k4 + 3], inv)) << 16);
-    *reinterpret_cast<uint2*>(orow + 8 * k4) = make_uint2(w0, w1);
-  }
+  uint16_t* orow = out + (((int64_t)r * q_len + jq) * Hq + hq) * kHD + 32 * (q >> 2) + 8 * (q & 3) + 4 * g;
+  const uint32_t w0 = (uint32_t)f2bf(__fmul_rn(O[0], inv)) | ((uint32_t)f2bf(__fmul_rn(O[1], inv)) << 16);
+  const uint32_t w1 = (uint32_t)f2bf(__fmul_rn(O[2], inv)) | ((uint32_t)f2bf(__fmul_rn(O[3], inv)) << 16);
+  *reinterpret_cast<uint2*>(orow) = make_uint2(w0, w1);
 }
 
 // fp32 path: one wave per (query row, query head, request).  Same chunking:
@@ -523,7 +519,7 @@ static biv_status launch_attn_bf16(const char* who, const void* q, int64_t q_str
                      seg_tokens, nseg_max, ws);
   biv_status st = launched(who);
   if (st != BIV_OK || nseg_max <= 1) return st;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(Hkv, R), dim3(256), 0, s, ctx, static_cast<uint16_t*>(out), q_len,
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(Hkv, R), dim3(kCombThreads), 0, s, ctx, static_cast<uint16_t*>(out), q_len,
                      Hq, Hkv, max_blocks, seg_tokens, nseg_max, ws);
   return launched(who);
 }

@@ -223,6 +223,42 @@ def test_rmsnorm_f32_and_mixed(biv):
     check_bf16(f64(y2), ref2, "rmsnorm f32->bf16")
 
 
+@pytest.mark.parametrize("H", [1024, 4096, 8192])
+def test_rmsnorm_vector_path_f32_residual(biv, H):
+    """The decoder's call: an fp32 residual stream normalised into bf16 (and
+    into fp32) through the 4-element vector path, on a ragged row count, with
+    row bits independent of M; a 16-byte-misaligned input takes the scalar
+    path and stays within the same bound."""
+    Mx = 300
+    x_np = wl.normal_f32(14 + H, (Mx, H), std=2.0)
+    g_np = wl.normal_f32(15 + H, (H,), std=0.1, mean=1.0)
+    gb = wl.bf16_bits(g_np)
+    x = dev_f32(x_np)
+    announce("rmsnorm vector path", H)
+    y = torch.empty((Mx, H), dtype=torch.bfloat16, device=DEV)
+    biv.rmsnorm_bi(x, dev_bf16(gb), y, 1e-6)
+    yf = torch.empty((Mx, H), dtype=torch.float32, device=DEV)
+    biv.rmsnorm_bi(x, dev_f32(g_np), yf, 1e-6)
+    sync()
+    check_bf16(f64(y), oracle.rmsnorm(x_np.astype(np.float64), oracle.as_f64(gb, "bf16"), 1e-6), "rmsnorm vec bf16")
+    check_f32(f64(yf), oracle.rmsnorm(x_np.astype(np.float64), g_np.astype(np.float64), 1e-6), axis=1,
+              what="rmsnorm vec f32")
+    full = bits(y)
+    for M in (1, 7, 64, 299):
+        yM = torch.empty((M, H), dtype=torch.bfloat16, device=DEV)
+        biv.rmsnorm_bi(x[:M].contiguous(), dev_bf16(gb), yM, 1e-6)
+        sync()
+        assert np.array_equal(bits(yM), full[:M]), f"rows changed at M={M}"
+    # misaligned rows (offset by one element) -> scalar path
+    buf = torch.empty(Mx * H + 1, dtype=torch.float32, device=DEV)
+    xm = buf[1:].view(Mx, H)
+    xm.copy_(x)
+    ym = torch.empty(Mx * H + 1, dtype=torch.bfloat16, device=DEV)[1:].view(Mx, H)
+    biv.rmsnorm_bi(xm, dev_bf16(gb), ym, 1e-6)
+    sync()
+    check_bf16(f64(ym), oracle.rmsnorm(x_np.astype(np.float64), oracle.as_f64(gb, "bf16"), 1e-6), "rmsnorm misaligned")
+
+
 # =====================================================================
 # gemm_bi
 # =====================================================================
