@@ -57,7 +57,7 @@ __device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp
 __device__ __forceinline__ int kv_swz(int k) { return ((k & 3) << 2) | ((k >> 2) & 3); }
 
 struct AttnWs {
-  float* part_o;   // [slot][64 values][64 lanes]
+  float* part_o;   // [slot][16 groups][64 lanes][4]: values 4q .. 4q+3 of a lane in group q
   float* part_ml;  // [slot][64 lanes][2]
 };
 
@@ -355,7 +355,10 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
   const int64_t slot = ((int64_t)r * Hkv + kvh) * nseg_max + seg;
   float* slot_o = ws.part_o + slot * 4096;
 #pragma unroll
-  for (int k = 0; k < 64; ++k) slot_o[k * 64 + lane] = Os[k];
+  for (int qg = 0; qg < 16; ++qg) {  // one 1 KiB streaming store per group of four values
+    const f32x4 w = {Os[4 * qg + 0], Os[4 * qg + 1], Os[4 * qg + 2], Os[4 * qg + 3]};
+    __builtin_nontemporal_store(w, reinterpret_cast<f32x4*>(slot_o + (qg * 64 + lane) * 4));
+  }
   ws.part_ml[slot * 128 + lane * 2 + 0] = Ms;
   ws.part_ml[slot * 128 + lane * 2 + 1] = Ls;
 }
@@ -387,8 +390,9 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(const int32_
     for (int b = 0; b < kCombBatch; ++b) {
       if (s0 + b < nseg) {
         const int64_t sl = slot0 + s0 + b;
+        const f32x4 w = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ws.part_o + sl * 4096) + q * 64 + lane);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) o[b][c] = __builtin_nontemporal_load(ws.part_o + sl * 4096 + (4 * q + c) * 64 + lane);
+        for (int c = 0; c < 4; ++c) o[b][c] = w[c];
         m[b] = ws.part_ml[sl * 128 + lane * 2 + 0];
         l[b] = ws.part_ml[sl * 128 + lane * 2 + 1];
       }
