@@ -44,7 +44,68 @@ def parse():
                         "Gumbel verify), one JSON line each, with rooflines, split-K/adaptive slowdowns and "
                         "oracle timings")
     p.add_argument("--iters", type=int, default=20, help="timed calls per point in --micro")
+    p.add_argument("--attn-only", action="store_true",
+                   help="only the pass's attention call (same contexts, pages and shapes) and a 512 MiB copy, "
+                        "--iters times each: the program the HBM traffic counters are collected on")
     return p.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "attn_decode_bi_traffic.json")
+ATTN_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "invariant_verify_verifier_amd", "csrc",
+                        "attention.hip")
+
+
+def _attn_source_hash():
+    import hashlib
+
+    with open(ATTN_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per attention launch from the rocprofv3 counter runs kept
+    under profiles/, or None when they were taken on another version of the
+    attention source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("attention_hip_sha256") != _attn_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def attn_only(args):
+    """The pass's attention call on its own: the 8B shapes, contexts
+    U[2048, 8192] (the pass's seeds), 16-token pages, K/V ~ N(0, 1) bf16; then
+    a plain 512 MiB device copy, the calibration for the byte counters."""
+    import torch
+
+    import invariant_verify_verifier_amd as biv
+    import workloads as wl
+
+    torch.cuda.set_device(0)
+    sh = wl.LLAMA3_8B
+    ctx = wl.context_lengths(wl.SEEDS["pass_len"], N_REQ, CTX_LO, CTX_HI)
+    lay = wl.paged_layout(ctx, K_CAND, seed=wl.SEEDS["pass_len"] + 1)
+    kc, vc = wl.device_kv_cache(sh, lay.num_blocks, wl.SEEDS["pass_kv"], layers=1)[0]
+    q = wl._torch_normal((N_REQ * K_CAND, sh.heads * sh.head_dim), wl.SEEDS["pass_kv"], 99, 1.0, "cuda",
+                         torch.bfloat16)
+    out = torch.empty((N_REQ * K_CAND, sh.heads, sh.head_dim), dtype=torch.bfloat16, device="cuda")
+    bt, cx = torch.from_numpy(lay.block_table).cuda(), torch.from_numpy(lay.ctx).cuda()
+    ws = torch.zeros(biv.attn_workspace_bytes(N_REQ, sh.kv_heads, lay.max_blocks), dtype=torch.uint8, device="cuda")
+    for _ in range(args.iters):
+        biv.attn_decode_bi(q, kc, vc, bt, cx, out, K_CAND, 1.0 / math.sqrt(sh.head_dim), ws)
+    src = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(args.iters):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    algo = float(np.sum(ctx.astype(np.int64) + K_CAND)) * sh.kv_heads * sh.head_dim * 2 * 2
+    print(json.dumps({"attn_only": True, "launches": args.iters, "algorithmic_bytes_per_launch": algo,
+                      "copy_bytes": 512 << 20, "attention_hip_sha256": _attn_source_hash()}), flush=True)
 
 
 class EventTimer:
@@ -413,6 +474,9 @@ def main():
     if args.micro and args.gpus == 1:
         micro(args)
         return
+    if args.attn_only and args.gpus == 1:
+        attn_only(args)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
               "(the verifier step shards by request with no inter-GPU traffic; see the design notes)",
@@ -491,7 +555,7 @@ def main():
                                "accept_len_differing": int((acc_var != acc_bi).sum())},
         "roofline": {"kernel": "attn_decode_bi (attn_bf16_kernel + attn_combine_kernel)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
                      "bytes_per_launch": attn_bytes, "avg_launch_ms": round(attn_ms, 5),
                      "launches_timed": len(timer.pairs)},
         "cpu_baseline": None,
