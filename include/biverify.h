@@ -153,7 +153,7 @@ biv_status gemm_bi(const void* A, const void* B, void* C, int64_t M, int64_t N, 
  * Calls that share a workspace must be ordered (same stream).
  * ------------------------------------------------------------------------ */
 #define BIV_ATTN_CHUNK_TOKENS 256
-#define BIV_ATTN_SEG_TOKENS 1024
+#define BIV_ATTN_SEG_TOKENS 2048
 
 size_t biv_attn_workspace_bytes(int R, int Hkv, int max_blocks, int seg_tokens);
 

@@ -9,22 +9,21 @@
 //
 // bf16 path.  The keys of a request are cut at fixed absolute positions:
 //   sub-tile = 32 keys (one MFMA block), chunk = 256 keys (the KV split),
-//   segment  = seg_tokens keys (1024 for the invariant kernel).
-// One workgroup of four waves per (segment, KV head, request).  Each wave
-// computes the partial (m, l, o) of one chunk for all rows of the KV head:
-// S^T = K Q^T and O^T = V^T P^T on the 32x32x16 bf16 MFMA, softmax statistics
-// in fp32 (log2 domain), rescaled sub-tile by sub-tile in ascending order.
-// The four chunk partials meet in LDS and are left-folded in ascending chunk
-// order into the segment result (each thread folds 16 of the 32 x 128
-// outputs); a segment longer than four chunks repeats this in rounds.
-// Segment results go to the workspace; a second, small kernel left-folds
-// them in ascending order and writes the output (a request with a single
-// segment is written directly).  A kernel boundary, not a device-wide fence,
-// makes the segment results visible: on gfx950 such a fence writes back and
-// invalidates the whole L2 of an XCD, once per workgroup.  The rows of one KV head (q_len positions x G query heads <= 32)
-// share one 32-row MFMA block, so the K/V of a page is read once for all of
-// them (the pages' tile rule: G x (1+D) rows per KV head, here G x K <= 32).
-// K/V pages move from HBM straight into LDS (gfx950 global_load_lds_dwordx4).
+//   segment  = seg_tokens keys (2048 for the invariant kernel).
+// One 64-lane wave per (segment, KV head, request), four per CU.  The rows
+// of one KV head (q_len positions x G query heads <= 32) share one 32-row
+// MFMA block, so the K/V of a page is read once for all of them (the pages'
+// tile rule: G x (1+D) rows per KV head, here G x K <= 32).  The wave streams
+// its segment's K and V sub-tiles from HBM straight into a ring of LDS slots
+// (gfx950 global_load_lds_dwordx4) and computes S^T = K Q^T and O^T = V^T P^T
+// on the 32x32x16 bf16 MFMA, softmax statistics in fp32 (log2 domain),
+// sub-tile by sub-tile in ascending order; each finished chunk's partial
+// (m, l, o) is left-folded into the segment result in registers.  Segment
+// results go to the workspace; a second, small kernel left-folds them in
+// ascending order and writes the output (a request with a single segment is
+// written directly).  A kernel boundary, not a device-wide fence, makes the
+// segment results visible: on gfx950 such a fence writes back and
+// invalidates the whole L2 of an XCD.
 //
 // Every boundary is an absolute position and every fold runs in ascending
 // order, so a row's bits depend only on its own query, its own request's KV
@@ -55,6 +54,8 @@ __device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp
 // reads (4 consecutive keys x 4 consecutive pieces per 32 lanes) both land on
 // distinct bank groups.
 __device__ __forceinline__ int kv_swz(int k) { return ((k & 3) << 2) | ((k >> 2) & 3); }
+
+__device__ __forceinline__ int pick_window(int w, int w0, int w1, int wx) { return w == 0 ? w0 : (w == 1 ? w1 : wx); }
 
 struct AttnWs {
   float* part_o;   // [slot][16 groups][64 lanes][4]: values 4q .. 4q+3 of a lane in group q
@@ -109,8 +110,9 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
   // loaded together: none depends on another, and the copies of the first
   // sub-tiles can only start once all three have landed.
   const int L = ctx[r];
-  int bt_w0 = -1;
+  int bt_w0 = -1, bt_w1 = -1;  // the segment's first two 64-page windows
   if (page0 + lane < max_blocks) bt_w0 = bt[page0 + lane];
+  if (seg_tokens > kPagesPerWin * 16 && page0 + kPagesPerWin + lane < max_blocks) bt_w1 = bt[page0 + kPagesPerWin + lane];
   // this lane's query row (MFMA column li)
   const bool row_ok = li < nrows;
   const int jq = row_ok ? li / G : 0;
@@ -146,8 +148,10 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
     const int lp = page0 + kPagesPerWin * w + lane;
     return window_ids(w, lp < n_pages ? bt[lp] : -1);
   };
-  int mypage = window_ids(0, bt_w0);
-  int win = 0;
+  // windows 0 and 1 are loaded at the start; a later window (segments
+  // longer than 2048 tokens) is loaded when the copies enter it
+  const int pw0 = window_ids(0, bt_w0), pw1 = window_ids(1, bt_w1);
+  int pwx = -1, winx = 1;
   uint32_t valid_q = 0;  // bits 2(s%16), 2(s%16)+1: pages of sub-tile s present
 
   // Direct-to-LDS copy of one sub-tile (32 keys) of K or V: 8 copies of
@@ -155,14 +159,21 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
   // window, i.e. row 4c + i/16, position i%16, so it fetches piece
   // (i%16) ^ kv_swz(row) of that key.  kv_swz(4c + i/16) = 4(i/16) + c%4.
   const unsigned voff0 = 256u * (lane >> 4) + 16u * ((lane & 15) ^ (4 * (lane >> 4)));
-  auto issue = [&](int j, int slot) {
-    const int s = j >> 1;
-    if (!(j & 1) && (s >> 5) != win) {  // K of the first sub-tile of a new window
-      win = s >> 5;
-      mypage = load_window(win);
+  // the window holding load j's pages (its register is passed by value to
+  // the copy: selecting between captured variables inside the lambda would
+  // force them into private memory)
+  auto window_for = [&](int j) {
+    const int w = (j >> 1) >> 5;
+    if (!(j & 1) && w > winx) {  // K of the first sub-tile of window w >= 2
+      winx = w;
+      pwx = load_window(w);
     }
-    const int p0 = __builtin_amdgcn_readlane(mypage, (2 * s) & 63);
-    const int p1 = __builtin_amdgcn_readlane(mypage, (2 * s + 1) & 63);
+    return w;
+  };
+  auto issue = [&](int j, int slot, int pv) {
+    const int s = j >> 1;
+    const int p0 = __builtin_amdgcn_readlane(pv, (2 * s) & 63);
+    const int p1 = __builtin_amdgcn_readlane(pv, (2 * s + 1) & 63);
     if (!(j & 1)) {
       const int sh = 2 * (s & 15);
       valid_q = (valid_q & ~(3u << sh)) | ((uint32_t)(p0 >= 0) << sh) | ((uint32_t)(p1 >= 0) << (sh + 1));
@@ -204,7 +215,10 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   // prologue: the first kRing loads
   const int n_pro = min(kRing, total);
-  for (int j = 0; j < n_pro; ++j) issue(j, j);
+  for (int j = 0; j < n_pro; ++j) {
+    const int w = window_for(j);
+    issue(j, j, pick_window(w, pw0, pw1, pwx));
+  }
 
   float Ms = -INFINITY, Ls = 0.0f, Os[64];
 #pragma unroll
@@ -233,7 +247,10 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
       sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[t], sacc, 0, 0, 0);
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // K slot read: refill it
-    if (2 * s + kRing < total) issue(2 * s + kRing, sk);
+    if (2 * s + kRing < total) {
+      const int w = window_for(2 * s + kRing);
+      issue(2 * s + kRing, sk, pick_window(w, pw0, pw1, pwx));
+    }
     // ---- softmax statistics of the sub-tile (log2 domain)
     // score v of the lane is key kk = 8(v/4) + 4g + v%4 of the sub-tile; it
     // is visible when kk <= last_key - sub_base and its page is present
@@ -315,7 +332,10 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
       }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // V slot read: refill it
-    if (2 * s + 1 + kRing < total) issue(2 * s + 1 + kRing, sv);
+    if (2 * s + 1 + kRing < total) {
+      const int w = window_for(2 * s + 1 + kRing);
+      issue(2 * s + 1 + kRing, sv, pick_window(w, pw0, pw1, pwx));
+    }
     sk = sk + 2 >= kRing ? sk + 2 - kRing : sk + 2;
     sv = sv + 2 >= kRing ? sv + 2 - kRing : sv + 2;
     // ---- end of a chunk: fold its partial into the segment result (ascending)

@@ -453,7 +453,9 @@ def _run_attn(biv, lay, kc, vc, q, q_len, dtype="bf16", fn=None, **kw):
     bt, cx = dev_i32(lay.block_table), dev_i32(lay.ctx)
     ws = None
     if dtype == "bf16":
-        nbytes = biv.attn_workspace_bytes(len(lay.ctx), kc.shape[1], lay.max_blocks, kw.pop("seg", 1024))
+        seg = kw.pop("seg", None)
+        nbytes = (biv.attn_workspace_bytes(len(lay.ctx), kc.shape[1], lay.max_blocks) if seg is None
+                  else biv.attn_workspace_bytes(len(lay.ctx), kc.shape[1], lay.max_blocks, seg))
         ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
     (fn or biv.attn_decode_bi)(dev(q), kcd, vcd, bt, cx, out, q_len, 1.0 / math.sqrt(D), ws, **kw)
     sync()
@@ -468,9 +470,9 @@ def _attn_ref(lay, kc, vc, q, q_len, dtype="bf16"):
 @pytest.mark.parametrize("q_len", [1, 8])
 def test_attention_bf16_parity(biv, q_len):
     """32 q heads / 8 KV heads x 128, paged KV (16-token pages, permuted),
-    contexts spanning several 256-token chunks and 1024-token segments plus
+    contexts spanning several 256-token chunks and 2048-token segments plus
     ragged tails and exact boundaries."""
-    ctx = [0, 255 - q_len + 1, 256, 1023, 1024, 1025, 2500, 5000]
+    ctx = [0, 255 - q_len + 1, 256, 1023, 1024, 1025, 2048 - q_len, 2049 - q_len, 2500, 5000]
     R = len(ctx)
     lay, kc, vc, q = _attn_inputs(R, q_len, 32, 8, 128, ctx, seed=50 + q_len)
     announce("attention bf16 parity q_len", q_len)
