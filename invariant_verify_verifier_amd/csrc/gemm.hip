@@ -412,14 +412,15 @@ static void launch_bf16(const void* A, const void* B, void* C, float* partial, i
 // Tile of the staged kernel for a weight with N outputs: one tiling per
 // weight shape, the same for every M.  (Each output's reduction order is the
 // same under every tile -- one MFMA shape, ascending k -- so the tile only
-// decides which workgroup computes which outputs.)  Chosen by measurement at
-// M = 512 on the decoder's weights.
+// decides which workgroup computes which outputs.)  Chosen by measurement:
+// at M = 512 on the decoder's weights, and for the 8192 <= N < 16384 class
+// (no decoder weight) across M = 1 .. 512.
 enum DmaTile { kTileL = 0, kTileS = 1, kTileQ = 2, kTileT = 3 };
 #ifndef BIV_GEMM_L_TILE
 #define BIV_GEMM_L_TILE 256, 256, 2, 2, 4  // BM, BN, stages, waves along M, waves along N
 #endif
 #ifndef BIV_GEMM_S_TILE
-#define BIV_GEMM_S_TILE 128, 128, 2, 2, 4
+#define BIV_GEMM_S_TILE 128, 64, 3, 4, 2
 #endif
 #ifndef BIV_GEMM_Q_TILE
 #define BIV_GEMM_Q_TILE 64, 128, 3, 2, 4
@@ -429,7 +430,7 @@ enum DmaTile { kTileL = 0, kTileS = 1, kTileQ = 2, kTileT = 3 };
 #endif
 static DmaTile dma_tile_for(int64_t N) {
   if (N >= 16384) return kTileL;  // 256 x 256, 8 waves of 128 x 64, 2 stages (128 KiB LDS)
-  if (N >= 8192) return kTileS;   // 128 x 128, 8 waves of 64 x 32, 2 stages (64 KiB)
+  if (N >= 8192) return kTileS;   // 128 x 64, 8 waves of 32 x 32, 3 stages (72 KiB)
   if (N > 4096) return kTileQ;    // 64 x 128, 8 waves of 32 x 32, 3 stages (72 KiB)
   return kTileT;                  // 128 x 64, 8 waves of 32 x 32, 4 stages (96 KiB)
 }
