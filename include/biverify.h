@@ -140,7 +140,8 @@ biv_status gemm_bi(const void* A, const void* B, void* C, int64_t M, int64_t N, 
  * row's result depends only on its own request's data and length.
  * Positions >= ctx[r] + q_len read as empty (values zero, keys masked).
  * Two launches: the chunk/segment pass, then (only when some request spans
- * more than one segment) the fold of the segment results.
+ * more than one segment) the fold of the segment results.  The fp32 path
+ * folds all chunk partials of a row in one ascending left fold (one launch).
  *
  * Supported: dt BIV_BF16 with D == 128 and q_len * (Hq/Hkv) <= 32 (bf16 MFMA
  * path); dt BIV_F32 with D in {64, 128} (fp32 path, any q_len).  Hq % Hkv == 0,

@@ -586,7 +586,7 @@ extern "C" int biv_attn_adaptive_split(int R, int Hkv, int max_blocks) {
   using namespace biv;
   if (R <= 0 || Hkv <= 0 || max_blocks <= 0) return kChunk;
   const int64_t cap = (int64_t)max_blocks * 16;
-  const int64_t want = cdiv(1024, (int64_t)R * Hkv);  // segments per (request, head) for 4 waves per CU
+  const int64_t want = cdiv(1024, (int64_t)R * Hkv);  // segments per (request, head): one wave per SIMD
   int64_t split = cdiv(cdiv(cap, want), kChunk) * kChunk;
   return (int)std::max<int64_t>(kChunk, split);
 }

@@ -6,14 +6,19 @@
 // afterwards (split-K); the batch-invariant matmul drops split-K and always
 // uses one and the same data-parallel tiling.
 //
-// bf16 path (gfx950 MFMA).  Workgroup tile 128 x 128 (M x N), K staged 64 at a
-// time through LDS (double buffered, 16-byte chunks XOR-swizzled by row so the
-// 128-bit fragment reads are bank-conflict free).  Four waves in a 2 x 2
-// arrangement each own 64 x 64 outputs as 2 x 2 blocks of the 32x32x16 bf16
-// MFMA.  Every output element is reduced by the same instruction over
+// bf16 path (gfx950 MFMA), two kernels with one per-element reduction:
+// every output element is reduced by the 32x32x16 bf16 MFMA over
 // k = 0, 16, 32, ... in ascending order with fp32 accumulators, so its bits
 // depend only on its own row of A and column of B: not on M, not on the tile
-// it lands in, not on the other rows.  The tiling is the same for every M.
+// it lands in, not on the other rows.  The tiling depends on the weight shape
+// alone and is the same for every M.
+//  - gemm_dma_kernel (K a multiple of 64, the decoder's case): A and B tiles
+//    copied HBM -> LDS by global_load_lds_dwordx4 into a ring of 64-wide k
+//    stages; tile shape and wave arrangement chosen per weight width (see
+//    dma_tile_for); store, residual-accumulate and SwiGLU epilogues.
+//  - gemm_bf16_kernel (any K % 8 == 0): 128 x 128 tiles, K staged 64 at a time
+//    through registers into double-buffered, XOR-swizzled LDS; four waves of
+//    64 x 64 outputs.
 //
 // Workgroup -> tile mapping is XCD aware: the dispatcher deals workgroups to
 // the 8 XCDs round-robin, so workgroup b is remapped to give each XCD a
@@ -145,8 +150,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(const uint16_t*
 // each stage's A (BM x 64) and B (BN x 64) tiles are copied HBM -> LDS by
 // global_load_lds_dwordx4 in 1 KiB windows of 8 rows x 128 B (whole 128-byte
 // lines: half-line rows move at roughly half the rate), STAGES - 1 stages in
-// flight ahead of the one being multiplied.  Four waves in a 2 x 2
-// arrangement own (BM/2) x (BN/2) outputs each.  The tile shape is chosen from
+// flight ahead of the one being multiplied.  WAVES_M x WAVES_N waves own
+// (BM/WAVES_M) x (BN/WAVES_N) outputs each.  The tile shape is chosen from
 // the weight shape (N) alone.
 constexpr int kDBK = 64;
 
