@@ -57,16 +57,23 @@ ATTN_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "invariant_v
 
 
 def _attn_source_hash():
+    """SHA-256 of the attention source with comments and whitespace removed:
+    it changes when the code does, not when a comment does."""
     import hashlib
+    import re
 
-    with open(ATTN_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    with open(ATTN_SRC) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    src = re.sub(r"\s+", " ", src).strip()
+    return hashlib.sha256(src.encode()).hexdigest()
 
 
 def recorded_traffic():
     """HBM bytes per attention launch from the rocprofv3 counter runs kept
     under profiles/, or None when they were taken on another version of the
-    attention source."""
+    attention code."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
