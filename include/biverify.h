@@ -222,6 +222,21 @@ biv_status biv_rope_table(float* cos_sin, int max_pos, int D, double theta);
 biv_status rope_apply(void* x, int64_t stride, const int32_t* pos, const float* cos_sin, int T,
                       int n_heads, int D, int max_pos, biv_dtype dt, biv_stream stream);
 
+/* rope_apply on the Q and K heads of a fused QKV output followed by
+ * kv_overwrite of its (rotated) K and V heads, in one pass over the rows
+ * (RoPE as above; the overwrite as in [LLM42] para 3).  qkv: T rows of at
+ * least (Hq + 2*Hkv)*D elements, `stride` elements apart: Q heads at element
+ * 0, K heads at Hq*D, V heads at (Hq+Hkv)*D; Q and K are rotated in place.
+ * pos, cos_sin, max_pos as for rope_apply; slot, k_cache, v_cache, num_blocks
+ * as for kv_overwrite.  Results are bit for bit those of
+ * rope_apply(qkv, stride, pos, cos_sin, T, Hq + Hkv, D, max_pos) followed by
+ * kv_overwrite(qkv + Hq*D, qkv + (Hq+Hkv)*D, stride, slot, ...).  bf16 rows
+ * with D a multiple of 16, stride a multiple of 8 and 16-byte aligned
+ * pointers take the fused kernel; anything else runs those two calls. */
+biv_status rope_kv_overwrite(void* qkv, int64_t stride, const int32_t* pos, const float* cos_sin,
+                             const int64_t* slot, void* k_cache, void* v_cache, int T, int Hq, int Hkv, int D,
+                             int max_pos, int num_blocks, biv_dtype dt, biv_stream stream);
+
 /* out[m, n] = silu(g) * u, silu(g) = g / (1 + exp(-g)), fp32 math; gu [M, 2N],
  * out [M, N], both in dt.  block == 0: g = gu[m, n], u = gu[m, N + n] (gate
  * and up halves); block > 0 (dividing N): the columns come in groups of

@@ -22,6 +22,7 @@ from ._lib import (  # noqa: F401
     pack_gate_up,
     rmsnorm_bi,
     rope_apply,
+    rope_kv_overwrite,
     rope_table,
     splitk_auto_splits,
     splitk_workspace_bytes,

@@ -45,6 +45,7 @@ _SIGS = {
     "embed_rows": ([_vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp], _i32),
     "biv_rope_table": ([_vp, _i32, _i32, _f64], _i32),
     "rope_apply": ([_vp, _i64, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp], _i32),
+    "rope_kv_overwrite": ([_vp, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp], _i32),
     "swiglu": ([_vp, _vp, _i64, _i64, _i64, _i32, _vp], _i32),
     "biv_splitk_workspace_bytes": ([_i64, _i64, _i32], _sz),
     "biv_splitk_auto_splits": ([_i64, _i64, _i64], _i32),
@@ -262,6 +263,24 @@ def rope_apply(x, pos, cos_sin, n_heads, D):
     assert pos.numel() == x.shape[0] and cos_sin.shape[1] * 2 == D
     _check("rope_apply", _lib.rope_apply(_p(x), x.stride(0), _p(pos), _p(cos_sin), x.shape[0], n_heads, D,
                                          cos_sin.shape[0], _dt(x), _stream()))
+
+
+def rope_kv_overwrite(qkv, pos, cos_sin, slot, k_cache, v_cache, n_q_heads):
+    """rope_apply on the Q and K heads of the fused QKV rows, then kv_overwrite
+    of their K and V heads, in one pass (same bits as the two calls)."""
+    T = qkv.shape[0]
+    num_blocks, Hkv, _, D = k_cache.shape
+    assert qkv.stride(-1) == 1 and qkv.shape[1] >= (n_q_heads + 2 * Hkv) * D
+    _same_dtype(qkv, k_cache, v_cache)
+    _contig(pos, cos_sin, slot, k_cache, v_cache)
+    _want(pos, torch.int32, "pos")
+    _want(cos_sin, torch.float32, "cos_sin")
+    _want(slot, torch.int64, "slot")
+    assert pos.numel() == T and slot.numel() == T and cos_sin.shape[1] * 2 == D
+    assert k_cache.shape == v_cache.shape
+    _check("rope_kv_overwrite", _lib.rope_kv_overwrite(_p(qkv), qkv.stride(0), _p(pos), _p(cos_sin), _p(slot),
+                                                       _p(k_cache), _p(v_cache), T, n_q_heads, Hkv, D,
+                                                       cos_sin.shape[0], num_blocks, _dt(qkv), _stream()))
 
 
 def swiglu(gu, out, block=0):

@@ -84,6 +84,65 @@ __global__ void rope_apply_kernel(void* __restrict__ x, int64_t stride, const in
   store_from_f32(x, ib, rb, dt);
 }
 
+// RoPE on the Q and K heads of a fused QKV row and the KV overwrite of its K
+// and V heads in one pass over the row: the same fp32 rotation as
+// rope_apply_kernel, rounded once to bf16; the rotated K goes both back to
+// the row and to the cache slot, V is a bit copy.  bf16 only.  One thread per
+// unit of a token: a group of 8 rotation pairs of a Q or K head (the 16 bytes
+// at i0 and the 16 at i0 + D/2), or a 16-byte piece of a V head.
+__global__ void rope_kv_vec_kernel(uint16_t* __restrict__ x, int64_t stride, const int32_t* __restrict__ pos,
+                                   const float* __restrict__ cos_sin, const int64_t* __restrict__ slot,
+                                   uint4* __restrict__ k_cache, uint4* __restrict__ v_cache, int T, int Hq, int Hkv,
+                                   int D, int max_pos, int64_t num_slots) {
+  const int half = D >> 1, groups = half >> 3, row16 = D >> 3;
+  const int rot_units = (Hq + Hkv) * groups;
+  const int per_tok = rot_units + Hkv * row16;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)T * per_tok) return;
+  const int t = (int)(gid / per_tok);
+  const int u = (int)(gid - (int64_t)t * per_tok);
+  uint16_t* row = x + (int64_t)t * stride;
+  const int64_t s = slot[t];
+  const bool to_cache = s >= 0 && s < num_slots;
+  const int64_t page = s >> 4, off = s & 15;
+  if (u < rot_units) {
+    const int h = u / groups, i0 = (u - h * groups) * 8;
+    uint4* pa = reinterpret_cast<uint4*>(row + (int64_t)h * D + i0);
+    uint4* pb = reinterpret_cast<uint4*>(row + (int64_t)h * D + half + i0);
+    uint4 a = *pa, b = *pb;
+    const int p = pos[t];
+    if (p >= 0 && p < max_pos) {
+      const float4* cs = reinterpret_cast<const float4*>(cos_sin + ((int64_t)p * half + i0) * 2);
+      uint32_t* aw = reinterpret_cast<uint32_t*>(&a);
+      uint32_t* bw = reinterpret_cast<uint32_t*>(&b);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 c2 = cs[q];  // (cos, sin) of pairs i0 + 2q and i0 + 2q + 1
+        const float a0 = __uint_as_float(aw[q] << 16), a1 = __uint_as_float(aw[q] & 0xffff0000u);
+        const float b0 = __uint_as_float(bw[q] << 16), b1 = __uint_as_float(bw[q] & 0xffff0000u);
+        const float ra0 = __fsub_rn(__fmul_rn(a0, c2.x), __fmul_rn(b0, c2.y));
+        const float rb0 = __fadd_rn(__fmul_rn(b0, c2.x), __fmul_rn(a0, c2.y));
+        const float ra1 = __fsub_rn(__fmul_rn(a1, c2.z), __fmul_rn(b1, c2.w));
+        const float rb1 = __fadd_rn(__fmul_rn(b1, c2.z), __fmul_rn(a1, c2.w));
+        aw[q] = (uint32_t)f2bf(ra0) | ((uint32_t)f2bf(ra1) << 16);
+        bw[q] = (uint32_t)f2bf(rb0) | ((uint32_t)f2bf(rb1) << 16);
+      }
+      *pa = a;
+      *pb = b;
+    }
+    if (h >= Hq && to_cache) {
+      uint4* dst = k_cache + ((page * Hkv + (h - Hq)) * 16 + off) * row16;
+      dst[i0 >> 3] = a;
+      dst[(half + i0) >> 3] = b;
+    }
+  } else if (to_cache) {
+    const int v = u - rot_units;
+    const int h = v / row16, piece = v - h * row16;
+    const uint4* src = reinterpret_cast<const uint4*>(row + (int64_t)(Hq + Hkv + h) * D);
+    v_cache[((page * Hkv + h) * 16 + off) * row16 + piece] = src[piece];
+  }
+}
+
 __global__ void swiglu_kernel(const void* __restrict__ gu, void* __restrict__ out, int64_t M, int64_t N, int64_t block,
                               int dt) {
   const int64_t total = M * N;
@@ -161,6 +220,37 @@ extern "C" biv_status rope_apply(void* x, int64_t stride, const int32_t* pos, co
   hipLaunchKernelGGL(rope_apply_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), x, stride, pos, cos_sin, T, n_heads, D, max_pos, (int)dt);
   return launched("rope_apply");
+}
+
+extern "C" biv_status rope_kv_overwrite(void* qkv, int64_t stride, const int32_t* pos, const float* cos_sin,
+                                        const int64_t* slot, void* k_cache, void* v_cache, int T, int Hq, int Hkv,
+                                        int D, int max_pos, int num_blocks, biv_dtype dt, biv_stream stream) {
+  using namespace biv;
+  BIV_REQUIRE(valid_dt(dt), "rope_kv_overwrite: bad dtype");
+  BIV_REQUIRE(T >= 0 && Hq >= 1 && Hkv >= 1 && D >= 2 && D % 2 == 0 && max_pos >= 1 && num_blocks >= 0,
+              "rope_kv_overwrite: bad sizes T=%d Hq=%d Hkv=%d D=%d", T, Hq, Hkv, D);
+  BIV_REQUIRE(stride >= (int64_t)(Hq + 2 * Hkv) * D, "rope_kv_overwrite: stride %lld < (Hq+2*Hkv)*D",
+              (long long)stride);
+  if (T == 0) return BIV_OK;
+  BIV_REQUIRE(qkv && pos && cos_sin && slot && k_cache && v_cache, "rope_kv_overwrite: NULL pointer");
+  const bool vec = dt == BIV_BF16 && D % 16 == 0 && stride % 8 == 0 && aligned16(qkv) && aligned16(cos_sin) &&
+                   aligned16(k_cache) && aligned16(v_cache);
+  if (!vec) {
+    // the two separate passes, same results
+    const biv_status r = rope_apply(qkv, stride, pos, cos_sin, T, Hq + Hkv, D, max_pos, dt, stream);
+    if (r != BIV_OK) return r;
+    const size_t es = dt_size(dt);
+    const char* base = static_cast<const char*>(qkv);
+    return kv_overwrite(base + (size_t)Hq * D * es, base + (size_t)(Hq + Hkv) * D * es, stride, slot, k_cache,
+                        v_cache, T, Hkv, D, num_blocks, dt, stream);
+  }
+  const int64_t per_tok = (int64_t)(Hq + Hkv) * (D / 16) + (int64_t)Hkv * (D / 8);
+  const int64_t n = (int64_t)T * per_tok;
+  hipLaunchKernelGGL(rope_kv_vec_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<uint16_t*>(qkv), stride, pos, cos_sin, slot,
+                     static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), T, Hq, Hkv, D, max_pos,
+                     (int64_t)num_blocks * 16);
+  return launched("rope_kv_overwrite");
 }
 
 extern "C" biv_status swiglu(const void* gu, void* out, int64_t M, int64_t N, int64_t block, biv_dtype dt,

@@ -154,14 +154,13 @@ class VerifierModel:
         scale = 1.0 / math.sqrt(sh.head_dim)
         gemm = gemm_fn or L.gemm_bi
         attend = attn_fn or L.attn_decode_bi
-        qc, kc = sh.q_cols, sh.kv_cols
+        qc = sh.q_cols
         L.embed_rows(tokens, self.embed, x)
         for li, lw in enumerate(self.layers):
             k_cache, v_cache = caches[li]
             L.rmsnorm_bi(x, lw["attn_norm"], h, sh.eps)
             gemm(h, lw["wqkv"], qkv)
-            L.rope_apply(qkv, pos, self.rope, sh.heads + sh.kv_heads, sh.head_dim)
-            L.kv_overwrite(qkv[:, qc:qc + kc], qkv[:, qc + kc:], slots, k_cache, v_cache)
+            L.rope_kv_overwrite(qkv, pos, self.rope, slots, k_cache, v_cache, sh.heads)
             attend(qkv[:, :qc], k_cache, v_cache, block_table, ctx, attn, q_len, scale, ws)
             gemm(attn.view(W, qc), lw["wo"], x, accumulate=True)
             L.rmsnorm_bi(x, lw["ffn_norm"], h, sh.eps)

@@ -65,6 +65,11 @@ def test_host_side_argument_errors(lib):
     assert lib.gumbel_verify(None, None, None, 0, 4, 8, None, None, None, None) == 0  # R = 0
     lib.kv_overwrite.argtypes = [vp, vp, i64, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     assert lib.kv_overwrite(None, None, 4, None, None, None, 1, 8, 128, 10, 1, None) == 1  # stride < Hkv*D
+    lib.rope_kv_overwrite.argtypes = [vp, i64, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
+    # stride < (Hq + 2*Hkv) * D
+    assert lib.rope_kv_overwrite(bp, 6000, bp, bp, bp, bp, bp, 1, 32, 8, 128, 16, 4, 1, None) == 1
+    assert lib.rope_kv_overwrite(bp, 6144, bp, bp, bp, bp, bp, 1, 32, 8, 127, 16, 4, 1, None) == 1  # odd D
+    assert lib.rope_kv_overwrite(None, 6144, None, None, None, None, None, 0, 32, 8, 128, 16, 4, 1, None) == 0
     lib.attn_decode_bi.argtypes = [vp, i64, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp,
                                    ctypes.c_size_t, vp]
     # Hq not a multiple of Hkv

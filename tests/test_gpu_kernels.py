@@ -172,6 +172,50 @@ def test_kv_overwrite_bitwise(biv, dtype):
     assert np.array_equal(bits(vc), vref.view(bits(vc).dtype))
 
 
+@pytest.mark.parametrize("dtype,extra_cols", [("bf16", 0), ("bf16", 8), ("bf16", 3), ("f32", 0)])
+def test_rope_kv_overwrite_matches_the_two_calls(biv, dtype, extra_cols):
+    """The fused RoPE + KV overwrite gives the bits of rope_apply followed by
+    kv_overwrite (Q and K rotated in the row, rotated K and raw V in the
+    cache), and both match the oracle; rows with a position outside the table
+    stay unrotated, slots outside the cache are skipped.  extra_cols pads the
+    row stride (3 makes bf16 rows unaligned, which takes the two-call path)."""
+    nb, Hq, Hkv, D, T = 41, 32, 8, 128, 67
+    width = (Hq + 2 * Hkv) * D + extra_cols
+    g = wl.rng(21)
+    slots = g.permutation(nb * 16)[:T].astype(np.int64)
+    slots[5], slots[60] = -3, nb * 16
+    pos = g.integers(0, 4096, size=T).astype(np.int32)
+    pos[9], pos[11] = -1, 4096
+    dev, mk = (dev_bf16, wl.normal_bf16) if dtype == "bf16" else (dev_f32, wl.normal_f32)
+    src_np = mk(22, (T, width))
+    kc_np, vc_np = mk(23, (nb, Hkv, 16, D)), mk(24, (nb, Hkv, 16, D))
+    table = biv.rope_table(4096, D, 500000.0).to(DEV)
+    x1, k1, v1 = dev(src_np), dev(kc_np), dev(vc_np)
+    x2, k2, v2 = dev(src_np), dev(kc_np), dev(vc_np)
+    ps, sl = dev_i32(pos), dev_i64(slots)
+    announce("rope_kv_overwrite", dtype, extra_cols)
+    biv.rope_kv_overwrite(x1, ps, table, sl, k1, v1, Hq)
+    biv.rope_apply(x2, ps, table, Hq + Hkv, D)
+    biv.kv_overwrite(x2[:, Hq * D:(Hq + Hkv) * D], x2[:, (Hq + Hkv) * D:(Hq + 2 * Hkv) * D], sl, k2, v2)
+    sync()
+    for a, b, what in [(x1, x2, "rows"), (k1, k2, "k cache"), (v1, v2, "v cache")]:
+        assert np.array_equal(bits(a), bits(b)), what
+    # oracle: rotate the rows in fp64, then overwrite the valid slots
+    ref = oracle.as_f64(src_np, dtype).copy()
+    ok_pos = (pos >= 0) & (pos < 4096)
+    rot = ref[ok_pos, :(Hq + Hkv) * D].reshape(-1, Hq + Hkv, D)
+    ref[ok_pos, :(Hq + Hkv) * D] = oracle.rope(rot, pos[ok_pos], 500000.0).reshape(-1, (Hq + Hkv) * D)
+    chk = (lambda g_, r, w: check_bf16(g_, r, w)) if dtype == "bf16" else (lambda g_, r, w: check_f32(g_, r, what=w))
+    chk(f64(x1), ref, "rotated rows")
+    ok = (slots >= 0) & (slots < nb * 16)
+    kref = oracle.as_f64(kc_np, dtype).copy()
+    vref = oracle.as_f64(vc_np, dtype).copy()
+    kn = f64(x1)[:, Hq * D:(Hq + Hkv) * D].reshape(T, Hkv, D)
+    vn = oracle.as_f64(src_np, dtype)[:, (Hq + Hkv) * D:(Hq + 2 * Hkv) * D].reshape(T, Hkv, D)
+    oracle.kv_overwrite(kref, vref, kn[ok], vn[ok], slots[ok])
+    assert np.array_equal(f64(k1), kref) and np.array_equal(f64(v1), vref)
+
+
 # =====================================================================
 # rmsnorm_bi
 # =====================================================================
