@@ -44,6 +44,10 @@ def parse():
                         "Gumbel verify), one JSON line each, with rooflines, split-K/adaptive slowdowns and "
                         "oracle timings")
     p.add_argument("--iters", type=int, default=20, help="timed calls per point in --micro")
+    p.add_argument("--dvr", action="store_true",
+                   help="instead of the pass: decode-verify-rollback at the pass's shape (split-K fast path, K=8, "
+                        "--rounds rounds) against one-token-at-a-time invariant decoding and the fast path alone")
+    p.add_argument("--rounds", type=int, default=3, help="verification rounds in --dvr")
     p.add_argument("--attn-only", action="store_true",
                    help="only the pass's attention call (same contexts, pages and shapes) and a 512 MiB copy, "
                         "--iters times each: the program the HBM traffic counters are collected on")
@@ -167,37 +171,6 @@ def setup(torch, n_layers):
     batch = V.make_batch(t0, cand, ctx, lay.block_table, noise)
     return dict(sh=sh, ctx=ctx, lay=lay, dw=dw, caches=caches, model=model, batch=batch, d=d, t0=t0, cand=cand,
                 noise=noise)
-
-
-class SplitVariants:
-    """The pass's GEMMs and attention swapped for their non-invariant
-    counterparts: split-K with the split count chosen from the shape
-    (gemm_splitk, auto) and attention with the KV split chosen from the load
-    (attn_decode_adaptive, auto).  Each owns its workspaces."""
-
-    def __init__(self, torch, biv, R, Hkv, max_blocks):
-        self.torch, self.biv = torch, biv
-        self.split = biv.attn_adaptive_split(R, Hkv, max_blocks)
-        self.attn_ws = torch.empty(max(biv.attn_workspace_bytes(R, Hkv, max_blocks, self.split), 16),
-                                   dtype=torch.uint8, device="cuda")
-        self.gemm_ws = {}
-        self.splits = {}
-
-    def gemm(self, a, b, c, accumulate=False):
-        M, K = a.shape
-        N = b.shape[0]
-        sp = self.biv.splitk_auto_splits(M, N, K)
-        self.splits[(N, K)] = sp
-        ws = self.gemm_ws.get((M, N, sp))
-        if ws is None:
-            ws = self.torch.empty(max(self.biv.splitk_workspace_bytes(M, N, sp), 16), dtype=self.torch.uint8,
-                                  device="cuda")
-            self.gemm_ws[(M, N, sp)] = ws
-        return self.biv.gemm_splitk(a, b, c, sp, ws, accumulate=accumulate)
-
-    def attn(self, q, k_cache, v_cache, block_table, ctx, out, q_len, scale, workspace=None):
-        return self.biv.attn_decode_adaptive(q, k_cache, v_cache, block_table, ctx, out, q_len, scale, self.attn_ws,
-                                             split_tokens=self.split)
 
 
 def time_passes(torch, model, batch, caches, steps, **kw):
@@ -476,10 +449,110 @@ def micro(args):
         torch.cuda.empty_cache()
 
 
+def dvr_bench(args):
+    """Decode-verify-rollback (LLM-42 post, paragraphs 3-4) at the pass's
+    shape: N = 64 requests, K = 8, contexts U[2048, 8192].  Three ways to
+    produce the same number of tokens per request, timed with HIP events:
+    the fast path alone (split-K GEMMs + adaptive attention splits, one token
+    per forward, not batch invariant), decode-verify-rollback (K fast-path
+    tokens, then one invariant verifier pass over all N*K), and
+    one-token-at-a-time decoding with the invariant kernels.  The committed
+    streams of the last two must be equal.  Gumbel noise for every (request,
+    position) the run can reach is made before the timed region."""
+    import torch
+
+    import workloads as wl
+    from invariant_verify_verifier_amd import dvr as D
+    from invariant_verify_verifier_amd import verifier as V
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    sh, K, R = wl.LLAMA3_8B, K_CAND, N_REQ
+    n_tok = args.rounds * K
+    # every sampled position lies in ctx+1 .. ctx+n_tok: a round starts after
+    # at most (rounds-1)*K committed tokens and samples K more
+    span = n_tok
+    ctx = wl.context_lengths(wl.SEEDS["pass_len"], R, CTX_LO, CTX_HI)
+    lay = wl.paged_layout(ctx, n_tok + K, seed=wl.SEEDS["pass_len"] + 1)
+    print(f"[bench] dvr setup: {args.layers} layers, {R} requests, K={K}, {args.rounds} rounds", file=sys.stderr,
+          flush=True)
+    dw = wl.device_model_weights(sh, wl.SEEDS["pass_weights"], layers=args.layers)
+    caches = wl.device_kv_cache(sh, lay.num_blocks, wl.SEEDS["pass_kv"], layers=args.layers)
+    shape = V.Shape(args.layers, sh.hidden, sh.heads, sh.kv_heads, sh.head_dim, sh.ffn, sh.vocab, sh.eps,
+                    sh.rope_theta)
+    model = V.VerifierModel(shape, torch.bfloat16, dw["layers"], dw["embed"], dw["lm_head"], dw["final_norm"],
+                            max_pos=16384)
+    t0 = wl.tokens(wl.SEEDS["pass_tokens"], (R,), sh.vocab)
+    table = torch.empty((R, span, sh.vocab), dtype=torch.float32, device="cuda")
+    for i in range(span):
+        table[:, i] = torch.from_numpy(wl.gumbel_noise(wl.SEEDS["pass_noise"], np.arange(R), ctx + 1 + i, sh.vocab))
+    print("[bench] dvr noise ready", file=sys.stderr, flush=True)
+    ctx_of = np.asarray(ctx, np.int64)
+
+    def noise_fn(req, pos):
+        req = np.asarray(req, np.int64)
+        off = np.asarray(pos, np.int64) - ctx_of[req] - 1
+        return table[torch.from_numpy(req).cuda(), torch.from_numpy(off).cuda()]
+
+    dvr = D.DecodeVerifyRollback(model, caches, lay.block_table, K, noise_fn, fast="split")
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        out = fn()
+        end.record()
+        torch.cuda.synchronize()
+        return out, start.elapsed_time(end) / 1e3
+
+    # warm-up: workspaces and buffers for both row counts
+    dvr.sequential(t0, ctx, 1)
+    dvr.sequential(t0, ctx, 1, **dvr.fast_kw)
+    dvr.verify(t0, np.zeros((R, K), np.int32), ctx)
+    print("[bench] dvr warm-up done", file=sys.stderr, flush=True)
+    inv_seq, t_inv = timed(lambda: dvr.sequential(t0, ctx, n_tok))
+    print(f"[bench] invariant decode: {t_inv:.3f} s", file=sys.stderr, flush=True)
+    fast_seq, t_fast = timed(lambda: dvr.sequential(t0, ctx, n_tok, **dvr.fast_kw))
+    print(f"[bench] fast-path decode: {t_fast:.3f} s", file=sys.stderr, flush=True)
+    dvr.stats = D.RoundStats()
+
+    hist, t_dvr = timed(lambda: dvr.run(t0, ctx, args.rounds))
+    print(f"[bench] decode-verify-rollback: {t_dvr:.3f} s", file=sys.stderr, flush=True)
+    n_dvr = sum(len(h) for h in hist)
+    equal = all(np.array_equal(np.asarray(h[:n_tok], np.int32), inv_seq[r, :len(h[:n_tok])])
+                for r, h in enumerate(hist))
+    v_dvr, v_inv, v_fast = n_dvr / t_dvr, R * n_tok / t_inv, R * n_tok / t_fast
+    line = {
+        "metric": "decode-verify-rollback committed tokens/s (1 GPU)",
+        "value": round(v_dvr, 2),
+        "unit": "committed tok/s",
+        "n_gpus": 1,
+        "steps": args.rounds,
+        "higher_is_better": True,
+        "dtype": "bf16",
+        "data": "synthetic (seeded random-init weights and KV of the stated shapes)",
+        "config": {"workload": f"Llama-3-8B-shaped decoder ({args.layers} layers), N = {R} requests, K = {K}, "
+                               "contexts U[2048,8192], fast path split-K + adaptive attention splits",
+                   "rounds": args.rounds, "tokens_per_request_baselines": n_tok},
+        "acceptance": round(dvr.stats.acceptance(K), 4),
+        "tokens_per_round": round(dvr.stats.tokens_per_round(), 3),
+        "committed_tokens": n_dvr,
+        "streams_equal_invariant_decode": bool(equal),
+        "all_invariant_decode_tok_s": round(v_inv, 2),
+        "fast_path_decode_tok_s": round(v_fast, 2),
+        "fast_path_streams_equal_invariant": int(sum(np.array_equal(fast_seq[r], inv_seq[r]) for r in range(R))),
+        "dvr_vs_all_invariant": round(v_dvr / v_inv, 4),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.micro and args.gpus == 1:
         micro(args)
+        return
+    if args.dvr and args.gpus == 1:
+        dvr_bench(args)
         return
     if args.attn_only and args.gpus == 1:
         attn_only(args)
@@ -525,7 +598,9 @@ def main():
     # the same pass with split-K GEMMs and load-adaptive attention splits
     # (not batch-invariant): slowdown = t_invariant / t_variant
     print("[bench] split-K / adaptive-split variant pass", file=sys.stderr, flush=True)
-    var = SplitVariants(torch, biv, N_REQ, env["sh"].kv_heads, env["lay"].max_blocks)
+    from invariant_verify_verifier_amd.dvr import SplitKernels
+
+    var = SplitKernels(N_REQ, env["sh"].kv_heads, env["lay"].max_blocks)
     model.verify(batch, caches, attn_fn=var.attn, gemm_fn=var.gemm)
     torch.cuda.synchronize()
     ms_var = time_passes(torch, model, batch, caches, args.steps, attn_fn=var.attn, gemm_fn=var.gemm)
