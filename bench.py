@@ -173,6 +173,24 @@ def setup(torch, n_layers):
                 noise=noise)
 
 
+def time_graph(torch, model, batch, caches, steps, warmup, **kw):
+    """The pass captured as one HIP graph: warm-up replays, then `steps`
+    replays between two events; ms per replay."""
+    graph = model.capture(batch, caches, **kw)
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        graph.replay()
+    end.record()
+    torch.cuda.synchronize()
+    del graph
+    return start.elapsed_time(end) / steps
+
+
 def time_passes(torch, model, batch, caches, steps, **kw):
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -578,22 +596,35 @@ def main():
     torch.cuda.synchronize()
     acc = batch.accept_len.cpu().numpy()
     assert np.array_equal(acc, env["d"]), f"planted divergence not recovered: {acc} vs {env['d']}"
-    print(f"[bench] warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
+    # eager passes with HIP events around every attention call (the roofline)
     timer.on = True
+    ms_eager = time_passes(torch, model, batch, caches, args.steps, attn_fn=attn)
+    timer.on = False
+    logits_eager = model.verify(batch, caches)[0].clone()
+    tgt_bi = batch.target.cpu().numpy().copy()
+    acc_bi = batch.accept_len.cpu().numpy().copy()
+    # the timed step: the whole pass replayed as one HIP graph
+    graph = model.capture(batch, caches)
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    logits_graph = model._buffers(batch.tokens.shape[0])["logits"]
+    assert torch.equal(logits_graph.view(torch.int32), logits_eager.view(torch.int32)), "graph replay changed logits"
+    assert np.array_equal(batch.target.cpu().numpy(), tgt_bi), "graph replay changed targets"
+    print(f"[bench] warmup done, timing {args.steps} graph replays", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record()
     for _ in range(args.steps):
-        model.verify(batch, caches, attn_fn=attn)
+        graph.replay()
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    timer.on = False
     ms_step = start.elapsed_time(end) / args.steps
-    tgt_bi = batch.target.cpu().numpy().copy()
-    acc_bi = batch.accept_len.cpu().numpy().copy()
+    assert np.array_equal(batch.accept_len.cpu().numpy(), acc_bi), "graph replay changed decisions"
+    del graph
     W = N_REQ * K_CAND
     # the same pass with split-K GEMMs and load-adaptive attention splits
     # (not batch-invariant): slowdown = t_invariant / t_variant
@@ -603,7 +634,7 @@ def main():
     var = SplitKernels(N_REQ, env["sh"].kv_heads, env["lay"].max_blocks)
     model.verify(batch, caches, attn_fn=var.attn, gemm_fn=var.gemm)
     torch.cuda.synchronize()
-    ms_var = time_passes(torch, model, batch, caches, args.steps, attn_fn=var.attn, gemm_fn=var.gemm)
+    ms_var = time_graph(torch, model, batch, caches, args.steps, args.warmup, attn_fn=var.attn, gemm_fn=var.gemm)
     tgt_var = batch.target.cpu().numpy()
     acc_var = batch.accept_len.cpu().numpy()
     value = W / (ms_step / 1e3)
@@ -619,6 +650,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_eager": round(ms_eager, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -628,6 +660,7 @@ def main():
                                "FFN 14336, vocab 128256), W = N*K = 64*8 = 512, contexts U[2048,8192], "
                                "16-token pages, Gumbel verify + KV overwrite",
                    "N": N_REQ, "K": K_CAND, "W": W, "ctx_mean": float(ctx.mean()),
+                   "launch": "whole pass captured as one HIP graph",
                    "wall_s_timed": round(wall, 3)},
         "slowdown_vs_splitk": {"value": round(ms_step / ms_var, 4), "ms_variant": round(ms_var, 4),
                                "variant": "gemm_splitk (auto splits per shape: "

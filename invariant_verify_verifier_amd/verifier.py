@@ -174,6 +174,24 @@ class VerifierModel:
         gemm(h, self.lm_head, logits)
         return logits
 
+    def capture(self, step, caches, **kw):
+        """Record one verifier step (forward + Gumbel verify) as a HIP graph.
+
+        The step's ~200 kernel launches then replay with no host work and no
+        launch gaps between them.  A replay reads the inputs from, and writes
+        the outputs to, the tensors of ``step``, the model's buffers and the
+        caches, so new data is written into those tensors in place before
+        ``graph.replay()``.  One eager step runs first so that every buffer and
+        workspace exists before the capture: the graph then holds kernel nodes
+        only (no kernel of the step allocates memory or clears it through the
+        runtime)."""
+        self.verify(step, caches, **kw)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.verify(step, caches, **kw)
+        return graph
+
     def verify(self, step, caches, **kw):
         """One verifier step.  `step` is a VerifyBatch already on the device.
         Returns (logits [W,V], target [R,K], accept_len [R], next_token [R])."""

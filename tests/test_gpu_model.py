@@ -297,3 +297,39 @@ def test_llama8b_slice_parity_planted_and_invariance(V):
         announce("8b slice alone", r)
         one = bits(model.verify(bb, caches)[0]).reshape(1, K, -1)
         assert np.array_equal(one[0], full[r])
+
+
+def test_llama8b_slice_graph_replay_matches_eager(V):
+    """The verifier step captured as one HIP graph replays to the eager step's
+    bits: logits, targets and decisions, on three replays with other eager
+    steps (another candidate batch over the same cache slots) and host
+    synchronisations between them."""
+    sh = wl.LLAMA3_8B
+    R, K = 4, 8
+    ctx = wl.context_lengths(52, R, 1500, 3000)
+    announce("8b slice graph setup", list(ctx))
+    _, _, model, lay, caches = _slice_world(V, ctx, seed=53)
+    t0 = wl.tokens(54, (R,), sh.vocab)
+    pos = ctx[:, None] + np.arange(K)[None, :] + 1
+    nz = wl.gumbel_noise(56, np.repeat(np.arange(R), K).reshape(R, K), pos, sh.vocab)
+    b = V.make_batch(t0, wl.tokens(55, (R, K), sh.vocab), ctx, lay.block_table, nz)
+    other = V.make_batch(t0, wl.tokens(57, (R, K), sh.vocab), ctx, lay.block_table, nz)
+    logits, tgt, acc, nxt = model.verify(b, caches)
+    sync()
+    ref = [bits(logits).copy(), tgt.cpu().numpy().copy(), acc.cpu().numpy().copy(), nxt.cpu().numpy().copy()]
+    announce("8b slice graph capture")
+    graph = model.capture(b, caches)
+    for i in range(3):
+        model.verify(other, caches)
+        sync()
+        announce("8b slice graph replay", i)
+        for t in (b.target, b.accept_len, b.next_token):
+            t.fill_(-7)
+        sync()
+        graph.replay()
+        sync()
+        got = [bits(model._buffers(R * K)["logits"]), b.target.cpu().numpy(), b.accept_len.cpu().numpy(),
+               b.next_token.cpu().numpy()]
+        for g_, r_, what in zip(got, ref, ["logits", "target", "accept_len", "next_token"]):
+            assert np.array_equal(g_, r_), f"replay {i}: {what}"
+    del graph
