@@ -596,20 +596,25 @@ def main():
     torch.cuda.synchronize()
     acc = batch.accept_len.cpu().numpy()
     assert np.array_equal(acc, env["d"]), f"planted divergence not recovered: {acc} vs {env['d']}"
-    # eager passes with HIP events around every attention call (the roofline)
-    timer.on = True
-    ms_eager = time_passes(torch, model, batch, caches, args.steps, attn_fn=attn)
-    timer.on = False
-    logits_eager = model.verify(batch, caches)[0].clone()
     tgt_bi = batch.target.cpu().numpy().copy()
     acc_bi = batch.accept_len.cpu().numpy().copy()
+    nxt_bi = batch.next_token.cpu().numpy().copy()
+    # the step as timed: lm_head and Gumbel verification fused (no logits in
+    # HBM); its decisions must be those of the unfused step, bit for bit
+    model.verify(batch, caches, fused_head=True)
+    torch.cuda.synchronize()
+    for got, ref, what in ((batch.target, tgt_bi, "targets"), (batch.accept_len, acc_bi, "accept_len"),
+                           (batch.next_token, nxt_bi, "next_token")):
+        assert np.array_equal(got.cpu().numpy(), ref), f"fused head changed {what}"
+    # eager passes with HIP events around every attention call (the roofline)
+    timer.on = True
+    ms_eager = time_passes(torch, model, batch, caches, args.steps, attn_fn=attn, fused_head=True)
+    timer.on = False
     # the timed step: the whole pass replayed as one HIP graph
-    graph = model.capture(batch, caches)
+    graph = model.capture(batch, caches, fused_head=True)
     for _ in range(args.warmup):
         graph.replay()
     torch.cuda.synchronize()
-    logits_graph = model._buffers(batch.tokens.shape[0])["logits"]
-    assert torch.equal(logits_graph.view(torch.int32), logits_eager.view(torch.int32)), "graph replay changed logits"
     assert np.array_equal(batch.target.cpu().numpy(), tgt_bi), "graph replay changed targets"
     print(f"[bench] warmup done, timing {args.steps} graph replays", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
@@ -632,9 +637,10 @@ def main():
     from invariant_verify_verifier_amd.dvr import SplitKernels
 
     var = SplitKernels(N_REQ, env["sh"].kv_heads, env["lay"].max_blocks)
-    model.verify(batch, caches, attn_fn=var.attn, gemm_fn=var.gemm)
+    model.verify(batch, caches, attn_fn=var.attn, gemm_fn=var.gemm, fused_head=True)
     torch.cuda.synchronize()
-    ms_var = time_graph(torch, model, batch, caches, args.steps, args.warmup, attn_fn=var.attn, gemm_fn=var.gemm)
+    ms_var = time_graph(torch, model, batch, caches, args.steps, args.warmup, attn_fn=var.attn, gemm_fn=var.gemm,
+                        fused_head=True)
     tgt_var = batch.target.cpu().numpy()
     acc_var = batch.accept_len.cpu().numpy()
     value = W / (ms_step / 1e3)
@@ -660,12 +666,13 @@ def main():
                                "FFN 14336, vocab 128256), W = N*K = 64*8 = 512, contexts U[2048,8192], "
                                "16-token pages, Gumbel verify + KV overwrite",
                    "N": N_REQ, "K": K_CAND, "W": W, "ctx_mean": float(ctx.mean()),
-                   "launch": "whole pass captured as one HIP graph",
+                   "launch": "whole pass captured as one HIP graph; lm_head + Gumbel verify fused",
                    "wall_s_timed": round(wall, 3)},
         "slowdown_vs_splitk": {"value": round(ms_step / ms_var, 4), "ms_variant": round(ms_var, 4),
                                "variant": "gemm_splitk (auto splits per shape: "
                                           + ", ".join(f"N={n},K={k}:{sp}" for (n, k), sp in sorted(var.splits.items()))
-                                          + f") + attn_decode_adaptive (split {var.split} tokens)",
+                                          + f") + attn_decode_adaptive (split {var.split} tokens); "
+                                          "same fused lm_head + Gumbel verify",
                                "target_rows_differing": int((tgt_var != tgt_bi).sum()),
                                "accept_len_differing": int((acc_var != acc_bi).sum())},
         "roofline": {"kernel": "attn_decode_bi (attn_bf16_kernel + attn_combine_kernel)", "bound": "hbm",

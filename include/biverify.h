@@ -183,6 +183,28 @@ biv_status gumbel_verify(const float* logits, const float* noise, const int32_t*
                          biv_stream stream);
 
 /* --------------------------------------------------------------------------
+ * lm_head_gumbel_verify — the lm_head matmul and gumbel_verify in one pass,
+ * without the fp32 logits in HBM (Gumbel post: argmax of logits + noise,
+ * then the candidate comparison; the noise is an input prepared in advance).
+ *
+ * h [R*K, H] bf16: final-normed hidden rows (row r*K + j as for gumbel_verify);
+ * w_head [V, H] bf16: the lm_head weight (gemm_bi's B layout); noise
+ * [R*K, V] fp32; cand [R, K] int32.  Scores are s = fl32(l + g) with l the
+ * fp32 result gemm_bi gives for the same h and w_head (same per-element
+ * reduction), so target, accept_len and next_token are bit for bit those of
+ * gemm_bi(h, w_head -> fp32 logits) followed by gumbel_verify.  H must be a
+ * multiple of 64, h and w_head 16-byte aligned.
+ * workspace: device memory of at least biv_gumbel_workspace_bytes(R*K, V)
+ * bytes, 8-byte aligned (per-row best pairs of each 64-column group); it need
+ * not be initialised, and calls that share it must not overlap.
+ * ------------------------------------------------------------------------ */
+size_t biv_gumbel_workspace_bytes(int M, int V);
+biv_status lm_head_gumbel_verify(const void* h, const void* w_head, const float* noise, const int32_t* cand,
+                                 int R, int K, int V, int H, int32_t* target, int32_t* accept_len,
+                                 int32_t* next_token, void* workspace, size_t workspace_bytes,
+                                 biv_stream stream);
+
+/* --------------------------------------------------------------------------
  * kv_overwrite — write the verifier's K/V into the slots the fast path wrote
  * ([LLM42] para 3: at every verification the fast path's KV, computed at some
  * other batch size, is overwritten with the verifier's consistent values).

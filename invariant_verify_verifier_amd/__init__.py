@@ -18,7 +18,9 @@ from ._lib import (  # noqa: F401
     gemm_bi,
     gemm_splitk,
     gumbel_verify,
+    gumbel_workspace_bytes,
     kv_overwrite,
+    lm_head_gumbel_verify,
     pack_gate_up,
     rmsnorm_bi,
     rope_apply,

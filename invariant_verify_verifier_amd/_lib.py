@@ -41,6 +41,8 @@ _SIGS = {
     "attn_decode_bi": ([_vp, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                         _vp, _sz, _vp], _i32),
     "gumbel_verify": ([_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp], _i32),
+    "biv_gumbel_workspace_bytes": ([_i32, _i32], _sz),
+    "lm_head_gumbel_verify": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
     "kv_overwrite": ([_vp, _vp, _i64, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp], _i32),
     "embed_rows": ([_vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp], _i32),
     "biv_rope_table": ([_vp, _i32, _i32, _f64], _i32),
@@ -220,6 +222,31 @@ def gumbel_verify(logits, noise, cand, target, accept_len, next_token):
     _check("gumbel_verify", _lib.gumbel_verify(_p(logits), _p(noise), _p(cand), R, K, V, _p(target),
                                                _p(accept_len), _p(next_token), _stream()))
     return target, accept_len, next_token
+
+
+def gumbel_workspace_bytes(M, V):
+    """Workspace bytes of lm_head_gumbel_verify for M = R*K rows and vocabulary V."""
+    return _lib.biv_gumbel_workspace_bytes(M, V)
+
+
+def lm_head_gumbel_verify(h, w_head, noise, cand, target, accept_len, next_token, workspace):
+    """lm_head matmul + Gumbel verification without fp32 logits in memory.
+    h [R*K, H] bf16, w_head [V, H] bf16, noise [R*K, V] fp32, cand/target
+    [R, K] int32, accept_len/next_token [R] int32; same results as gemm_bi to
+    fp32 logits followed by gumbel_verify."""
+    _contig(h, w_head, noise, cand, target, accept_len, next_token, workspace)
+    _want(h, torch.bfloat16, "h")
+    _want(w_head, torch.bfloat16, "w_head")
+    _want(noise, torch.float32, "noise")
+    for t, n in ((cand, "cand"), (target, "target"), (accept_len, "accept_len"), (next_token, "next_token")):
+        _want(t, torch.int32, n)
+    R, K = cand.shape
+    V, H = w_head.shape
+    assert tuple(h.shape) == (R * K, H) and noise.numel() == R * K * V
+    assert target.numel() == R * K and accept_len.numel() == R and next_token.numel() == R
+    _check("lm_head_gumbel_verify", _lib.lm_head_gumbel_verify(
+        _p(h), _p(w_head), _p(noise), _p(cand), R, K, V, H, _p(target), _p(accept_len), _p(next_token),
+        _p(workspace), workspace.numel() * workspace.element_size(), _stream()))
 
 
 def kv_overwrite(k_new, v_new, slot, k_cache, v_cache):

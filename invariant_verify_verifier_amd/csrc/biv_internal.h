@@ -107,4 +107,21 @@ __device__ __forceinline__ void lds_dma16(const void* sbase, unsigned voff, void
 
 __device__ __forceinline__ void vm_wait0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Gumbel-max pair order: the larger score wins, equal scores go to the lower
+// index, a NaN score never wins.  The order is associative and commutative,
+// so any grouping of a row's entries yields the same pair.
+__device__ __forceinline__ void take_better(float& bv, int& bi, float v, int i) {
+  v = (v != v) ? -INFINITY : v;
+  const bool better = (v > bv) | ((v == bv) & (i < bi));  // selects, no branch
+  bv = better ? v : bv;
+  bi = better ? i : bi;
+}
+
+// Second half of the fused lm_head + Gumbel verification: reduce the
+// per-group (score bits, index) pairs `part` [M][groups] of each row to its
+// target, then the accepted prefix and correction of each request
+// (verify.hip).
+biv_status launch_gumbel_finish(const uint2* part, int groups, const int32_t* cand, int R, int K,
+                                int32_t* target, int32_t* accept_len, int32_t* next_token, hipStream_t s);
+
 }  // namespace biv

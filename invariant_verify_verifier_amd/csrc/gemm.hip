@@ -31,6 +31,9 @@
 namespace biv {
 
 constexpr int kBM = 128, kBN = 128, kBK = 64;
+// Internal epilogue of the staged kernel (not a gemm_bi epilogue): Gumbel-max
+// of each row over each wave's columns, for lm_head_gumbel_verify.
+constexpr int kEpiGumbel = 3;
 constexpr int kGemmThreads = 256;
 constexpr int kTileBytes = kBM * kBK * 2;  // 16 KiB per operand tile
 
@@ -178,6 +181,26 @@ __device__ __forceinline__ void vm_wait_stages(int ahead) {  // ahead in [0, kMa
   }
 }
 
+// One reduce-scatter step of the Gumbel epilogue over lane offset O: keep
+// HALF of the rows (the upper half when bit O of the lane is set), fold in the
+// partner lane's copy of them.
+template <int O, int HALF>
+__device__ __forceinline__ void gumbel_fold_step(float* bv, int* bi, int li) {
+  const bool up = (li & O) != 0;
+#pragma unroll
+  for (int k = 0; k < HALF; ++k) {
+    const float send_v = up ? bv[k] : bv[k + HALF];
+    const int send_i = up ? bi[k] : bi[k + HALF];
+    float keep_v = up ? bv[k + HALF] : bv[k];
+    int keep_i = up ? bi[k + HALF] : bi[k];
+    const float rv = __shfl_xor(send_v, O, 64);
+    const int ri = __shfl_xor(send_i, O, 64);
+    take_better(keep_v, keep_i, rv, ri);
+    bv[k] = keep_v;
+    bi[k] = keep_i;
+  }
+}
+
 template <int BM, int BN, int STAGES, int WAVES_M, int WAVES_N, int OUT_DT, int EPI, bool kSplit>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_kernel(const uint16_t* __restrict__ A,
                                                        const uint16_t* __restrict__ B, void* C,
@@ -294,6 +317,62 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_kernel(const 
   }
 
   // 32x32 accumulator layout: lane holds column li; value v is row 8(v/4) + 4g + v%4.
+  if constexpr (EPI == kEpiGumbel) {
+    // C is the noise [M, N] fp32; `partial` receives, per row m and per
+    // group of WN columns (this wave's), the best (score bits, index) pair
+    // of s = fl32(acc + noise) under take_better's order: the same scores as
+    // storing the fp32 product and adding the noise afterwards.  Branch
+    // free: rows past M read row M-1 and are not written; columns past N
+    // enter as (-inf, INT_MAX), which never beats a real entry.
+    static_assert(!kSplit && OUT_DT == BIV_F32, "Gumbel epilogue: fp32 scores, no split");
+    const float* noise = static_cast<const float*>(C);
+    uint2* part = reinterpret_cast<uint2*>(partial);
+    const int groups = (N + WN - 1) / WN;
+    const int ncol0 = n0 + wn * WN;
+    if (ncol0 < N) {
+      const int grp = ncol0 / WN;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        float bv[16];
+        int bi[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          bv[v] = -INFINITY;
+          bi[v] = 0x7fffffff;
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = min(m0 + wm * WM + 32 * i + 8 * (v >> 2) + 4 * g + (v & 3), M - 1);
+          const float* nrow = noise + (int64_t)m * N;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int n = ncol0 + 32 * j + li;
+            const bool ok = n < N;
+            const float sc = acc[i][j][v] + nrow[ok ? n : N - 1];
+            take_better(bv[v], bi[v], ok ? sc : -INFINITY, ok ? n : 0x7fffffff);
+          }
+        }
+        // The 32 lanes of each half hold the same 16 rows.  Reduce-scatter:
+        // at offset o a lane keeps half of its rows (the upper half if bit o
+        // of its lane is set) and folds in its partner's copy of them, so
+        // after offsets 16, 8, 4, 2 lane li holds row li >> 1 over 16 lanes,
+        // and offset 1 completes it (31 exchanges instead of 80).
+        gumbel_fold_step<16, 8>(bv, bi, li);
+        gumbel_fold_step<8, 4>(bv, bi, li);
+        gumbel_fold_step<4, 2>(bv, bi, li);
+        gumbel_fold_step<2, 1>(bv, bi, li);
+        {
+          const float rv = __shfl_xor(bv[0], 1, 64);
+          const int ri = __shfl_xor(bi[0], 1, 64);
+          take_better(bv[0], bi[0], rv, ri);
+        }
+        const int v = li >> 1;
+        const int m = m0 + wm * WM + 32 * i + 8 * (v >> 2) + 4 * g + (v & 3);
+        if ((li & 1) == 0 && m < M) part[(int64_t)m * groups + grp] = make_uint2(__float_as_uint(bv[0]), (unsigned)bi[0]);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -433,6 +512,14 @@ enum DmaTile { kTileL = 0, kTileS = 1, kTileQ = 2, kTileT = 3 };
 #ifndef BIV_GEMM_T_TILE
 #define BIV_GEMM_T_TILE 128, 64, 4, 4, 2
 #endif
+// Columns per wave of a tile: the group width of the Gumbel epilogue's
+// per-row partial results (lm_head_gumbel_verify runs the L tile).
+template <int BM, int BN, int STAGES, int WAVES_M, int WAVES_N>
+constexpr int wave_cols() {
+  return BN / WAVES_N;
+}
+constexpr int kGumbelGroup = wave_cols<BIV_GEMM_L_TILE>();
+
 static DmaTile dma_tile_for(int64_t N) {
   if (N >= 16384) return kTileL;  // 256 x 256, 8 waves of 128 x 64, 2 stages (128 KiB LDS)
   if (N >= 8192) return kTileS;   // 128 x 64, 8 waves of 32 x 32, 3 stages (72 KiB)
@@ -596,4 +683,36 @@ extern "C" biv_status gemm_splitk(const void* A, const void* B, void* C, int64_t
     else hipLaunchKernelGGL((splitk_reduce_kernel<BIV_F32, BIV_EPI_STORE>), dim3(blocks), dim3(256), 0, s, part, C, MN, sp);
   }
   return launched("gemm_splitk/reduce");
+}
+
+extern "C" size_t biv_gumbel_workspace_bytes(int M, int V) {
+  using namespace biv;
+  if (M <= 0 || V <= 0) return 0;
+  return (size_t)M * (size_t)((V + kGumbelGroup - 1) / kGumbelGroup) * 8;
+}
+
+extern "C" biv_status lm_head_gumbel_verify(const void* h, const void* w_head, const float* noise, const int32_t* cand,
+                                            int R, int K, int V, int H, int32_t* target, int32_t* accept_len,
+                                            int32_t* next_token, void* workspace, size_t workspace_bytes,
+                                            biv_stream stream) {
+  using namespace biv;
+  BIV_REQUIRE(R >= 0 && K >= 1 && V >= 1 && H >= 1, "lm_head_gumbel_verify: need R >= 0, K >= 1, V >= 1, H >= 1");
+  BIV_REQUIRE((int64_t)R * K <= (1 << 30) && V <= (1 << 30), "lm_head_gumbel_verify: size too large");
+  BIV_REQUIRE(H % kDBK == 0 && (int64_t)H * 2 * 16 <= 0x7fffffff,
+              "lm_head_gumbel_verify: H must be a multiple of %d (H=%d)", kDBK, H);
+  if (R == 0) return BIV_OK;
+  BIV_REQUIRE(h && w_head && noise && cand && target && accept_len && next_token && workspace,
+              "lm_head_gumbel_verify: NULL pointer");
+  BIV_REQUIRE(aligned16(h) && aligned16(w_head), "lm_head_gumbel_verify: h and w_head must be 16-byte aligned");
+  BIV_REQUIRE(((uintptr_t)workspace & 7) == 0, "lm_head_gumbel_verify: workspace must be 8-byte aligned");
+  const int M = R * K;
+  BIV_REQUIRE(workspace_bytes >= biv_gumbel_workspace_bytes(M, V),
+              "lm_head_gumbel_verify: workspace %zu < %zu bytes", workspace_bytes, biv_gumbel_workspace_bytes(M, V));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  launch_dma_t<BIV_GEMM_L_TILE, BIV_F32, kEpiGumbel, false>(h, w_head, const_cast<float*>(noise),
+                                                           static_cast<float*>(workspace), M, V, H, 1, H, s);
+  const biv_status st = launched("lm_head_gumbel_verify/gemm");
+  if (st != BIV_OK) return st;
+  return launch_gumbel_finish(static_cast<const uint2*>(workspace), (V + kGumbelGroup - 1) / kGumbelGroup, cand, R, K, target,
+                              accept_len, next_token, s);
 }

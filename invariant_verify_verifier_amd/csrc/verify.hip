@@ -17,14 +17,6 @@ namespace biv {
 
 constexpr int kVerifyThreads = 1024;
 
-__device__ __forceinline__ void take_better(float& bv, int& bi, float v, int i) {
-  v = (v != v) ? -INFINITY : v;  // NaN never wins
-  if (v > bv || (v == bv && i < bi)) {
-    bv = v;
-    bi = i;
-  }
-}
-
 template <bool kVec4>
 __global__ __launch_bounds__(kVerifyThreads) void gumbel_argmax_kernel(const float* __restrict__ logits,
                                                                        const float* __restrict__ noise,
@@ -87,6 +79,38 @@ __global__ __launch_bounds__(kVerifyThreads) void gumbel_argmax_kernel(const flo
   }
 }
 
+// One workgroup per row: fold the row's per-group best pairs (written by the
+// lm_head GEMM's Gumbel epilogue) into its target.
+__global__ __launch_bounds__(256) void gumbel_groups_kernel(const uint2* __restrict__ part, int groups,
+                                                          int32_t* __restrict__ target) {
+  const int64_t row = blockIdx.x;
+  const uint2* pr = part + row * (int64_t)groups;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int i = threadIdx.x; i < groups; i += 256) {
+    const uint2 p = pr[i];
+    take_better(bv, bi, __uint_as_float(p.x), (int)p.y);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float ov = __shfl_xor(bv, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    take_better(bv, bi, ov, oi);
+  }
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sv[wave] = bv;
+    si[wave] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w) take_better(bv, bi, sv[w], si[w]);
+    target[row] = bi;
+  }
+}
+
 __global__ void verify_decide_kernel(const int32_t* __restrict__ target, const int32_t* __restrict__ cand,
                                      int R, int K, int32_t* __restrict__ accept_len,
                                      int32_t* __restrict__ next_token) {
@@ -103,6 +127,16 @@ __global__ void verify_decide_kernel(const int32_t* __restrict__ target, const i
   }
   accept_len[r] = a;
   next_token[r] = nx;
+}
+
+biv_status launch_gumbel_finish(const uint2* part, int groups, const int32_t* cand, int R, int K,
+                                int32_t* target, int32_t* accept_len, int32_t* next_token, hipStream_t s) {
+  hipLaunchKernelGGL(gumbel_groups_kernel, dim3((unsigned)(R * K)), dim3(256), 0, s, part, groups, target);
+  const biv_status st = launched("lm_head_gumbel_verify/groups");
+  if (st != BIV_OK) return st;
+  hipLaunchKernelGGL(verify_decide_kernel, dim3((R + 63) / 64), dim3(64), 0, s, target, cand, R, K, accept_len,
+                     next_token);
+  return launched("lm_head_gumbel_verify/decide");
 }
 
 }  // namespace biv

@@ -81,6 +81,7 @@ class VerifierModel:
         self.rope = L.rope_table(max_pos, shape.head_dim, shape.rope_theta).to(device)
         self._bufs = {}
         self._ws = {}
+        self._gumbel_ws = {}
 
     # ------------------------------------------------------------ construction
 
@@ -142,9 +143,10 @@ class VerifierModel:
 
     # ------------------------------------------------------------ forward
 
-    def forward(self, tokens, pos, ctx, q_len, block_table, slots, caches, attn_fn=None, gemm_fn=None):
+    def forward(self, tokens, pos, ctx, q_len, block_table, slots, caches, attn_fn=None, gemm_fn=None, head=True):
         """tokens/pos [W] int32, ctx [R] int32, block_table [R, mb] int32, slots [W] int64 (device).
-        Returns fp32 logits [W, V] (a buffer reused by the next call with the same W)."""
+        Returns fp32 logits [W, V] (a buffer reused by the next call with the same W), or with
+        head=False the final-normed hidden rows [W, H] that the lm_head would multiply."""
         sh = self.shape
         W = tokens.shape[0]
         R, mb = block_table.shape
@@ -171,6 +173,8 @@ class VerifierModel:
                 L.swiglu(gu, act, block=L.SWIGLU_BLOCK)
             gemm(act, lw["w_down"], x, accumulate=True)
         L.rmsnorm_bi(x, self.final_norm, h, sh.eps)
+        if not head:
+            return h
         gemm(h, self.lm_head, logits)
         return logits
 
@@ -192,9 +196,28 @@ class VerifierModel:
             self.verify(step, caches, **kw)
         return graph
 
-    def verify(self, step, caches, **kw):
+    def verify(self, step, caches, fused_head=False, **kw):
         """One verifier step.  `step` is a VerifyBatch already on the device.
-        Returns (logits [W,V], target [R,K], accept_len [R], next_token [R])."""
+        Returns (logits [W,V], target [R,K], accept_len [R], next_token [R]).
+        fused_head=True (bf16 model): the lm_head matmul and the Gumbel
+        verification run as one call that never stores the logits (the same
+        decisions as the invariant lm_head + gumbel_verify, bit for bit);
+        logits is then None.  The fused lm_head is the invariant one whatever
+        ``gemm_fn`` the layers use."""
+        if fused_head:
+            if self.dtype != torch.bfloat16:
+                raise ValueError("fused_head needs the bf16 model")
+            h = self.forward(step.tokens, step.pos, step.ctx, step.K, step.block_table, step.slots, caches,
+                             head=False, **kw)
+            W = h.shape[0]
+            ws = self._gumbel_ws.get(W)
+            if ws is None:
+                ws = torch.empty(L.gumbel_workspace_bytes(W, self.shape.vocab), dtype=torch.uint8,
+                                 device=self.device)
+                self._gumbel_ws[W] = ws
+            L.lm_head_gumbel_verify(h, self.lm_head, step.noise, step.cand, step.target, step.accept_len,
+                                    step.next_token, ws)
+            return None, step.target, step.accept_len, step.next_token
         logits = self.forward(step.tokens, step.pos, step.ctx, step.K, step.block_table, step.slots, caches, **kw)
         L.gumbel_verify(logits, step.noise, step.cand, step.target, step.accept_len, step.next_token)
         return logits, step.target, step.accept_len, step.next_token

@@ -65,6 +65,17 @@ def test_host_side_argument_errors(lib):
     assert lib.gumbel_verify(None, None, None, 0, 4, 8, None, None, None, None) == 0  # R = 0
     lib.kv_overwrite.argtypes = [vp, vp, i64, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     assert lib.kv_overwrite(None, None, 4, None, None, None, 1, 8, 128, 10, 1, None) == 1  # stride < Hkv*D
+    lib.lm_head_gumbel_verify.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.biv_gumbel_workspace_bytes.argtypes = [i32, i32]
+    lib.biv_gumbel_workspace_bytes.restype = ctypes.c_size_t
+    assert lib.biv_gumbel_workspace_bytes(512, 128256) == 512 * 2004 * 8
+    assert lib.biv_gumbel_workspace_bytes(3, 65) == 3 * 2 * 8
+    # H not a multiple of 64
+    assert lib.lm_head_gumbel_verify(bp, bp, bp, bp, 2, 4, 1000, 100, bp, bp, bp, bp, 1 << 20, None) == 1
+    # workspace too small
+    assert lib.lm_head_gumbel_verify(bp, bp, bp, bp, 2, 4, 1000, 128, bp, bp, bp, bp, 8, None) == 1
+    assert b"workspace" in lib.biv_last_error()
+    assert lib.lm_head_gumbel_verify(None, None, None, None, 0, 4, 1000, 128, None, None, None, None, 0, None) == 0
     lib.rope_kv_overwrite.argtypes = [vp, i64, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
     # stride < (Hq + 2*Hkv) * D
     assert lib.rope_kv_overwrite(bp, 6000, bp, bp, bp, bp, bp, 1, 32, 8, 128, 16, 4, 1, None) == 1

@@ -136,6 +136,60 @@ def test_gumbel_verify_nan_inf_rows(biv):
 
 
 # =====================================================================
+# lm_head_gumbel_verify (lm_head matmul with the Gumbel argmax in its epilogue)
+# =====================================================================
+
+
+@pytest.mark.parametrize("R,K,V", [(5, 8, 128256), (3, 3, 50021)])
+def test_lm_head_gumbel_verify_bitwise(biv, R, K, V):
+    """The fused call gives the bits of gemm_bi (fp32 logits) + gumbel_verify,
+    and both equal the oracle's rule applied to the GPU's logits.  Planted in
+    the noise: an exact tie at 1e9 between two columns in different 256-column
+    tiles (the lower index must win), NaNs at a row's best entries, an
+    all-NaN row (target 0), and -inf entries.  V = 50021 leaves a ragged last
+    tile and group; M = R*K rows leave a ragged last row tile."""
+    H = 4096
+    M = R * K
+    h = dev_bf16(wl.normal_bf16(120 + V % 5, (M, H)))
+    w = dev_bf16(wl.normal_bf16(121, (V, H), std=0.02))
+    logits = torch.empty((M, V), dtype=torch.float32, device=DEV)
+    announce("lm_head_gumbel_verify: unfused logits", R, K, V)
+    biv.gemm_bi(h, w, logits)
+    sync()
+    l32 = logits.cpu().numpy()
+    g = wl.gumbel_noise(122, np.repeat(np.arange(R), K).reshape(R, K),
+                        np.tile(np.arange(K) + 300, (R, 1)), V).reshape(M, V)
+    c1, c2 = 77, V - 200  # different 256-column tiles and 64-column groups
+    g[3, c1] = g[3, c2] = np.float32(1e9)  # |logit| << ulp(1e9) / 2: both scores are exactly 1e9
+    best = np.argsort(l32[5] + g[5])[-3:]
+    g[5, best] = np.nan  # the row's three best entries can never win
+    g[min(7, M - 1), :] = np.nan  # all-NaN row: target 0
+    g[1, ::3] = -np.inf
+    s_ref, _, _ = oracle.gumbel_verify(l32.reshape(R, K, V), g.reshape(R, K, V), np.zeros((R, K), np.int32))
+    assert s_ref[3 // K, 3 % K] == c1 and s_ref[min(7, M - 1) // K, min(7, M - 1) % K] == 0
+    d = wl.rng(123).integers(0, K + 1, size=R)
+    cand = wl.plant_divergence(s_ref, d, V, 124)
+    t_ref, a_ref, n_ref = oracle.gumbel_verify(l32.reshape(R, K, V), g.reshape(R, K, V), cand)
+    assert np.array_equal(a_ref, d)
+    outs = []
+    for fused in (False, True):
+        tgt = torch.full((R, K), -5, dtype=torch.int32, device=DEV)
+        acc = torch.full((R,), -5, dtype=torch.int32, device=DEV)
+        nxt = torch.full((R,), -5, dtype=torch.int32, device=DEV)
+        gd = dev_f32(g)
+        announce("lm_head_gumbel_verify fused" if fused else "gumbel_verify on the logits", R, K, V)
+        if fused:
+            ws = torch.empty(biv.gumbel_workspace_bytes(M, V), dtype=torch.uint8, device=DEV)
+            biv.lm_head_gumbel_verify(h, w, gd, dev_i32(cand), tgt, acc, nxt, ws)
+        else:
+            biv.gumbel_verify(logits, gd, dev_i32(cand), tgt, acc, nxt)
+        sync()
+        outs.append((tgt.cpu().numpy(), acc.cpu().numpy(), nxt.cpu().numpy()))
+    for got in outs:
+        assert np.array_equal(got[0], t_ref) and np.array_equal(got[1], a_ref) and np.array_equal(got[2], n_ref)
+
+
+# =====================================================================
 # kv_overwrite
 # =====================================================================
 

@@ -333,3 +333,23 @@ def test_llama8b_slice_graph_replay_matches_eager(V):
         for g_, r_, what in zip(got, ref, ["logits", "target", "accept_len", "next_token"]):
             assert np.array_equal(g_, r_), f"replay {i}: {what}"
     del graph
+    # the fused lm_head + Gumbel verification gives the same decisions, eager
+    # and replayed
+    announce("8b slice fused head")
+    _, ftgt, facc, fnxt = model.verify(b, caches, fused_head=True)
+    sync()
+    for g_, r_, what in zip([ftgt.cpu().numpy(), facc.cpu().numpy(), fnxt.cpu().numpy()], ref[1:],
+                            ["target", "accept_len", "next_token"]):
+        assert np.array_equal(g_, r_), f"fused head: {what}"
+    fgraph = model.capture(b, caches, fused_head=True)
+    for i in range(2):
+        model.verify(other, caches)
+        for t in (b.target, b.accept_len, b.next_token):
+            t.fill_(-7)
+        sync()
+        fgraph.replay()
+        sync()
+        for g_, r_, what in zip([b.target.cpu().numpy(), b.accept_len.cpu().numpy(), b.next_token.cpu().numpy()],
+                                ref[1:], ["target", "accept_len", "next_token"]):
+            assert np.array_equal(g_, r_), f"fused head replay {i}: {what}"
+    del fgraph
