@@ -507,7 +507,7 @@ enum DmaTile { kTileL = 0, kTileS = 1, kTileQ = 2, kTileT = 3 };
 #define BIV_GEMM_S_TILE 128, 64, 3, 4, 2
 #endif
 #ifndef BIV_GEMM_Q_TILE
-#define BIV_GEMM_Q_TILE 64, 128, 3, 2, 4
+#define BIV_GEMM_Q_TILE 128, 96, 4, 4, 1
 #endif
 #ifndef BIV_GEMM_T_TILE
 #define BIV_GEMM_T_TILE 128, 64, 4, 4, 2
@@ -523,7 +523,7 @@ constexpr int kGumbelGroup = wave_cols<BIV_GEMM_L_TILE>();
 static DmaTile dma_tile_for(int64_t N) {
   if (N >= 16384) return kTileL;  // 256 x 256, 8 waves of 128 x 64, 2 stages (128 KiB LDS)
   if (N >= 8192) return kTileS;   // 128 x 64, 8 waves of 32 x 32, 3 stages (72 KiB)
-  if (N > 4096) return kTileQ;    // 64 x 128, 8 waves of 32 x 32, 3 stages (72 KiB)
+  if (N > 4096) return kTileQ;    // 128 x 96, 4 waves of 32 x 96, 4 stages (112 KiB)
   return kTileT;                  // 128 x 64, 8 waves of 32 x 32, 4 stages (96 KiB)
 }
 

@@ -468,6 +468,30 @@ def test_gemm_swiglu_epilogue_ragged_and_unfused_layout(biv):
     check_f32(f64(c2), ref, axis=1, what="swiglu unfused over the packed weight")
 
 
+@pytest.mark.parametrize("N", [4096, 6144, 6184, 28672])
+def test_gemm_bf16_tile_classes_invariance(biv, N):
+    """Each weight-width class of the staged kernel (its own tile: N <= 4096,
+    4096 < N < 8192 with 6184 ragged against the tile, N >= 16384), K = 4096:
+    parity with the oracle at M = 333 (ragged rows), and every row's bits the
+    same for M = 1, 7, 64, 333 as inside M = 512."""
+    K = 4096
+    a_np = wl.normal_bf16(130, (512, K))
+    w_np = wl.normal_bf16(131 + N % 7, (N, K), std=0.02)
+    a, w = dev_bf16(a_np), dev_bf16(w_np)
+    announce("gemm bf16 tile class", N)
+    full = torch.empty((512, N), dtype=torch.float32, device=DEV)
+    biv.gemm_bi(a, w, full)
+    sync()
+    full_bits = bits(full)
+    ref = oracle.linear(oracle.as_f64(a_np[:333], "bf16"), oracle.as_f64(w_np, "bf16"))
+    check_f32(f64(full)[:333], ref, axis=1, what=f"gemm N={N}")
+    for M in (1, 7, 64, 333):
+        cM = torch.empty((M, N), dtype=torch.float32, device=DEV)
+        biv.gemm_bi(a[:M].contiguous(), w, cM)
+        sync()
+        assert np.array_equal(bits(cM), full_bits[:M]), f"rows changed at M={M}, N={N}"
+
+
 @pytest.mark.parametrize("M,N,K", [(77, 200, 264), (1, 130, 8), (129, 257, 1000), (300, 128, 4096)])
 def test_gemm_bf16_ragged_shapes(biv, M, N, K):
     a_np = wl.normal_bf16(20 + M, (M, K))
