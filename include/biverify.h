@@ -140,7 +140,8 @@ biv_status gemm_bi(const void* A, const void* B, void* C, int64_t M, int64_t N, 
  * row's result depends only on its own request's data and length.
  * Positions >= ctx[r] + q_len read as empty (values zero, keys masked).
  * Two launches: the chunk/segment pass, then (only when some request spans
- * more than one segment) the fold of the segment results.  The fp32 path
+ * more than one segment) the fold of the segment results; large grids add
+ * a one-workgroup launch before them that orders the segments.  The fp32 path
  * folds all chunk partials of a row in one ascending left fold (one launch).
  *
  * Supported: dt BIV_BF16 with D == 128 and q_len * (Hq/Hkv) <= 32 (bf16 MFMA
@@ -150,7 +151,9 @@ biv_status gemm_bi(const void* A, const void* B, void* C, int64_t M, int64_t N, 
  * workspace: device memory of at least
  * biv_attn_workspace_bytes(R, Hkv, max_blocks, BIV_ATTN_SEG_TOKENS) bytes,
  * 16-byte aligned (bf16 path; may be NULL for the fp32 path); it holds the
- * segment results between the two launches and needs no initialisation.
+ * segment results between the two launches and, for grids of at least four
+ * rounds of resident waves, the work list that launches the segments in
+ * longest-first order (same results); it needs no initialisation.
  * Calls that share a workspace must be ordered (same stream).
  * ------------------------------------------------------------------------ */
 #define BIV_ATTN_CHUNK_TOKENS 256

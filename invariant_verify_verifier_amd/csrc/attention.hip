@@ -98,9 +98,22 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx,
     uint16_t* __restrict__ out, int q_len, int Hq, int Hkv, int max_blocks, int num_blocks, float scale_log2,
-    int seg_tokens, int nseg_max, AttnWs ws) {
+    int seg_tokens, int nseg_max, AttnWs ws, const int32_t* __restrict__ items) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kRing * kSlot];
-  const int seg = blockIdx.x, kvh = blockIdx.y, r = blockIdx.z;
+  // grid: (segment, KV head, request), or with a work list a 1-D grid of
+  // (list entry, KV head), KV head fastest; an entry is r * nseg_max + seg
+  int seg, kvh, r;
+  if (items != nullptr) {
+    kvh = (int)(blockIdx.x % (unsigned)Hkv);
+    const int e = items[blockIdx.x / (unsigned)Hkv];
+    if (e < 0) return;
+    r = e / nseg_max;
+    seg = e - r * nseg_max;
+  } else {
+    seg = blockIdx.x;
+    kvh = blockIdx.y;
+    r = blockIdx.z;
+  }
   const int lane = threadIdx.x, g = lane >> 5, li = lane & 31;
   const int G = Hq / Hkv, nrows = q_len * G;
   const int32_t* bt = block_table + (int64_t)r * max_blocks;
@@ -383,6 +396,72 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
   ws.part_ml[slot * 128 + lane * 2 + 1] = Ls;
 }
 
+// Work list for large grids: every full segment first, then the partial last
+// segments, longest first, so that the dispatcher's list scheduling leaves
+// the short items for the end of the grid (LPT order).  Only the order of
+// the work changes: each item's arithmetic and its workspace slot are fixed
+// by (request, segment), so the results are the same bits.  One workgroup;
+// partial lengths are bucketed in 128 classes.
+__global__ __launch_bounds__(1024) void attn_plan_kernel(const int32_t* __restrict__ ctx, int R, int q_len,
+                                                        int max_blocks, int seg_tokens, int nseg_max,
+                                                        int32_t* __restrict__ items) {
+  constexpr int NB = 128;
+  __shared__ int n_full, full_cur, bucket_cnt[NB], bucket_start[NB], bucket_cur[NB];
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    n_full = 0;
+    full_cur = 0;
+  }
+  if (tid < NB) {
+    bucket_cnt[tid] = 0;
+    bucket_cur[tid] = 0;
+  }
+  __syncthreads();
+  const int cap = max_blocks * 16;
+  const int bw = (seg_tokens + NB - 1) / NB;
+  for (int r = tid; r < R; r += 1024) {
+    const int nt = min(ctx[r] + q_len, cap);
+    const int full = nt / seg_tokens, part = nt - full * seg_tokens;
+    atomicAdd(&n_full, full);
+    if (part > 0) atomicAdd(&bucket_cnt[(part - 1) / bw], 1);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int acc = n_full;
+    for (int b = NB - 1; b >= 0; --b) {
+      bucket_start[b] = acc;
+      acc += bucket_cnt[b];
+    }
+  }
+  __syncthreads();
+  for (int r = tid; r < R; r += 1024) {
+    const int nt = min(ctx[r] + q_len, cap);
+    const int full = nt / seg_tokens, part = nt - full * seg_tokens;
+    const int base = atomicAdd(&full_cur, full);
+    for (int k = 0; k < full; ++k) items[base + k] = r * nseg_max + k;
+    if (part > 0) {
+      const int b = (part - 1) / bw;
+      items[bucket_start[b] + atomicAdd(&bucket_cur[b], 1)] = r * nseg_max + full;
+    }
+  }
+  const int n_items = bucket_start[0] + bucket_cnt[0];
+  for (int i = n_items + tid; i < R * nseg_max; i += 1024) items[i] = -1;
+}
+
+// Waves of the segment kernel resident at once on the current device (four
+// per CU: its LDS ring takes a quarter of a CU's 160 KiB).
+static int resident_attn_waves() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1024;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cached[dev] = 4 * cus;
+  }
+  return cached[dev];
+}
+
 // Second pass for requests with more than one segment: left-fold the segment
 // results in ascending order (the fold above, element by element) and write
 // the output.  One workgroup of 1024 threads per (KV head, request); thread t
@@ -537,10 +616,23 @@ static biv_status launch_attn_bf16(const char* who, const void* q, int64_t q_str
   AttnWs ws;
   ws.part_o = static_cast<float*>(workspace);
   ws.part_ml = ws.part_o + (size_t)R * Hkv * nseg_max * 4096;
-  hipLaunchKernelGGL(attn_bf16_kernel, dim3(nseg_max, Hkv, R), dim3(64), 0, s, static_cast<const uint16_t*>(q), q_stride,
+  // A grid of at least four rounds of resident waves is launched in LPT
+  // order from a work list (decided by the call's shape alone).
+  const int64_t waves = (int64_t)R * nseg_max * Hkv;
+  int32_t* items = nullptr;
+  dim3 grid(nseg_max, Hkv, R);
+  if (waves >= 4 * (int64_t)resident_attn_waves() && waves <= 0x7fffffff) {
+    items = reinterpret_cast<int32_t*>(ws.part_ml + (size_t)R * Hkv * nseg_max * 128);
+    hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, s, ctx, R, q_len, max_blocks, seg_tokens, nseg_max,
+                       items);
+    biv_status st = launched(who);
+    if (st != BIV_OK) return st;
+    grid = dim3((unsigned)waves);
+  }
+  hipLaunchKernelGGL(attn_bf16_kernel, grid, dim3(64), 0, s, static_cast<const uint16_t*>(q), q_stride,
                      static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache), block_table, ctx,
                      static_cast<uint16_t*>(out), q_len, Hq, Hkv, max_blocks, num_blocks, scale * kLog2e,
-                     seg_tokens, nseg_max, ws);
+                     seg_tokens, nseg_max, ws, items);
   biv_status st = launched(who);
   if (st != BIV_OK || nseg_max <= 1) return st;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(Hkv, R), dim3(kCombThreads), 0, s, ctx, static_cast<uint16_t*>(out), q_len,
@@ -554,7 +646,8 @@ extern "C" size_t biv_attn_workspace_bytes(int R, int Hkv, int max_blocks, int s
   using namespace biv;
   if (R <= 0 || Hkv <= 0 || max_blocks <= 0 || seg_tokens <= 0) return 0;
   const size_t nseg = (size_t)cdiv((int64_t)max_blocks * 16, seg_tokens);
-  return (size_t)R * Hkv * nseg * (4096 + 128) * sizeof(float);
+  // segment results, then the work list of large grids (R * nseg entries)
+  return (size_t)R * Hkv * nseg * (4096 + 128) * sizeof(float) + (size_t)R * nseg * sizeof(int32_t);
 }
 
 extern "C" biv_status attn_decode_bi(const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,

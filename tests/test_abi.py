@@ -98,7 +98,7 @@ def test_workspace_sizes(lib):
     lib.biv_attn_workspace_bytes.argtypes = [ctypes.c_int] * 4
     n = lib.biv_attn_workspace_bytes(64, 8, 513, 1024)
     nseg = -(-513 * 16 // 1024)
-    assert n == 64 * 8 * nseg * (4096 + 128) * 4
+    assert n == 64 * 8 * nseg * (4096 + 128) * 4 + 64 * nseg * 4  # segment results + work list
     lib.biv_splitk_auto_splits.restype = ctypes.c_int
     lib.biv_splitk_auto_splits.argtypes = [ctypes.c_int64] * 3
     assert lib.biv_splitk_auto_splits(1, 14336, 4096) > 1  # small M -> split K
