@@ -28,6 +28,7 @@ from .ops import (  # noqa: F401
     attention,
     decoder_forward,
     gumbel_sample,
+    gumbel_topk,
     gumbel_verify,
     kv_overwrite,
     linear,

@@ -183,6 +183,22 @@ def gumbel_verify(logits32, noise32, cand):
     return target, accept, nxt
 
 
+def gumbel_topk(logits32, noise32, k):
+    """Top-k of the perturbed scores (Gumbel post, Gumbel-max paragraph: top-k
+    sampling comes out of the trick for free, with a pointer to "Stochastic
+    Beams and Where to Find Them"): the k largest s = fl32(logit + g) of a row
+    are k draws without replacement from the softmax.
+
+    logits32, noise32: [..., V] fp32.  Returns (idx [..., k] int32, score
+    [..., k] fp32): scores in descending order, equal scores in ascending
+    index order; a NaN score counts as -inf (so it comes last).
+    """
+    s = perturbed_scores(logits32, noise32)
+    s = np.where(np.isnan(s), np.float32(-np.inf), s)
+    order = np.argsort(-s, axis=-1, kind="stable")[..., :k]  # stable: equal scores keep index order
+    return order.astype(np.int32), np.take_along_axis(s, order, axis=-1)
+
+
 def rollback(ctx, accept, nxt, cand):
     """Host bookkeeping after a verification (LLM-42 post, paragraph 3: roll
     back and fix).  Committed tokens: cand[:a] plus next (a < K); all K when

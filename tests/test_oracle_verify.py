@@ -162,3 +162,44 @@ def test_tile_rule_golden():
         D = tile // G - 1
         assert G * (1 + D) <= tile < G * (2 + D)
         assert D == case["drafts"]
+
+
+@pytest.mark.parametrize("logits", [[0.3, -1.0, 2.0, 0.1], [1.0, 1.0, 1.0, 1.0]])
+def test_gumbel_topk_is_sampling_without_replacement(logits):
+    """Gumbel-top-k (the Gumbel post's "top-k for free"): the first two entries
+    of the top-2 of l + g are an ordered draw without replacement from the
+    softmax, P(a, b) = p_a p_b / (1 - p_a).  200k noise rows; chi-square over
+    the 12 ordered pairs, p > 1e-3.  Ascending order, a reused draw, or a second
+    entry taken from the wrong distribution all fail."""
+    V, n = len(logits), 200_000
+    g = wl.gumbel_noise(seed=9, requests=np.zeros(n, dtype=np.int64), positions=np.arange(n), vocab_size=V)
+    l32 = np.broadcast_to(np.asarray(logits, dtype=np.float32), (n, V))
+    idx, score = oracle.gumbel_topk(l32, g, 2)
+    assert (idx[:, 0] != idx[:, 1]).all() and (score[:, 0] >= score[:, 1]).all()
+    p = _softmax(logits)
+    pairs = [(a, b) for a in range(V) for b in range(V) if a != b]
+    expect = np.array([p[a] * p[b] / (1 - p[a]) for a, b in pairs]) * n
+    code = idx[:, 0] * V + idx[:, 1]
+    obs = np.array([(code == a * V + b).sum() for a, b in pairs])
+    assert obs.sum() == n
+    _, pval = stats.chisquare(obs, expect)
+    assert pval > 1e-3, (obs, expect, pval)
+
+
+def test_gumbel_topk_order_ties_nan_and_k1():
+    """Descending scores, equal scores in index order, NaN after every real
+    score (as -inf, in index order); k = 1 is the Gumbel-max target."""
+    l = np.array([[3, 1, 3, np.nan, -np.inf, 3, 2, np.nan]], dtype=np.float32)
+    g = np.zeros_like(l)
+    idx, score = oracle.gumbel_topk(l, g, 8)
+    assert list(idx[0]) == [0, 2, 5, 6, 1, 3, 4, 7]
+    assert list(score[0, :5]) == [3, 3, 3, 2, 1] and np.isneginf(score[0, 5:]).all()
+    allnan = np.full((1, 5), np.nan, np.float32)
+    assert list(oracle.gumbel_topk(allnan, np.zeros_like(allnan), 3)[0][0]) == [0, 1, 2]
+    R, K, V = 6, 4, 700
+    lr = wl.normal_f32(31, (R, K, V), std=2.0)
+    gr = wl.gumbel_noise(34, np.repeat(np.arange(R), K), np.tile(np.arange(K), R), V).reshape(R, K, V)
+    lr[0, 0, 5] = lr[0, 0, 9] = np.float32(1e9)  # exact tie
+    t, _, _ = oracle.gumbel_verify(lr, gr, np.zeros((R, K), np.int32))
+    top1, _ = oracle.gumbel_topk(lr, gr, 1)
+    assert np.array_equal(top1[..., 0], t) and t[0, 0] == 5
