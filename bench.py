@@ -437,13 +437,27 @@ def micro_verify(torch, biv, iters):
     t_roof = byts / (HBM_PEAK_GBS * 1e9) * 1e3
     print(f"[micro] gumbel_verify: {t_gpu * 1e3:.1f} us (roof {t_roof * 1e3:.1f}), oracle {t_cpu:.2f} s",
           file=sys.stderr, flush=True)
+    # Gumbel top-8 of the same rows (k draws without replacement per row)
+    KT = 8
+    t = time.perf_counter()
+    o_idx, o_sc = oracle.gumbel_topk(logits.reshape(R * K, V), noise.reshape(R * K, V), KT)
+    t_cpu_k = time.perf_counter() - t
+    ix = torch.empty((R * K, KT), dtype=torch.int32, device="cuda")
+    sc = torch.empty((R * K, KT), dtype=torch.float32, device="cuda")
+    t_gpu_k, p90_k = _event_times(torch, lambda i: biv.gumbel_topk(lg, nz, ix, sc), iters)
+    exact_k = bool(np.array_equal(ix.cpu().numpy(), o_idx) and
+                   np.array_equal(sc.cpu().numpy().view(np.uint32), o_sc.astype(np.float32).view(np.uint32)))
+    print(f"[micro] gumbel_topk k={KT}: {t_gpu_k * 1e3:.1f} us, oracle {t_cpu_k:.2f} s", file=sys.stderr, flush=True)
     return {"workload": "gumbel_verify: logits [64,8,128256] fp32 ~N(0,9), seeded Gumbel noise table, planted "
                         "first divergence d ~ U{0..8}",
             "ms": round(t_gpu, 5), "ms_p90": round(p90, 5), "roofline_ms": round(t_roof, 5),
             "frac": round(t_roof / t_gpu, 4), "rows_per_s": round(R * K / (t_gpu * 1e-3), 1),
             "bitwise_equal_to_oracle": exact,
             "cpu_oracle": {"kind": "oracle", "threads": _threads(), "s": round(t_cpu, 4),
-                           "rows_per_s": round(R * K / t_cpu, 1)}}
+                           "rows_per_s": round(R * K / t_cpu, 1)},
+            "topk": {"k": KT, "ms": round(t_gpu_k, 5), "ms_p90": round(p90_k, 5), "roofline_ms": round(t_roof, 5),
+                     "frac": round(t_roof / t_gpu_k, 4), "bitwise_equal_to_oracle": exact_k,
+                     "cpu_oracle": {"kind": "oracle", "threads": _threads(), "s": round(t_cpu_k, 4)}}}
 
 
 def _threads():

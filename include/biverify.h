@@ -186,6 +186,20 @@ biv_status gumbel_verify(const float* logits, const float* noise, const int32_t*
                          biv_stream stream);
 
 /* --------------------------------------------------------------------------
+ * gumbel_topk — the k largest perturbed scores of each row (Gumbel post: the
+ * Gumbel-max trick gives top-k sampling for free; the top k of l + g are k
+ * draws without replacement from the softmax).
+ *
+ * logits, noise [rows, V] fp32; idx [rows, k] int32: the indices in
+ * descending order of s = fl32(l + g), equal scores in ascending index order,
+ * a NaN score counted as -inf; score [rows, k] fp32 (nullable): those scores
+ * (NaN as -inf).  k = 1 gives gumbel_verify's targets.  1 <= k <= V;
+ * k > 8 returns BIV_EUNSUPPORTED.
+ * ------------------------------------------------------------------------ */
+biv_status gumbel_topk(const float* logits, const float* noise, int rows, int V, int k, int32_t* idx,
+                       float* score, biv_stream stream);
+
+/* --------------------------------------------------------------------------
  * lm_head_gumbel_verify — the lm_head matmul and gumbel_verify in one pass,
  * without the fp32 logits in HBM (Gumbel post: argmax of logits + noise,
  * then the candidate comparison; the noise is an input prepared in advance).

@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     exported_symbols,
     gemm_bi,
     gemm_splitk,
+    gumbel_topk,
     gumbel_verify,
     gumbel_workspace_bytes,
     kv_overwrite,

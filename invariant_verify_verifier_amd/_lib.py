@@ -41,6 +41,7 @@ _SIGS = {
     "attn_decode_bi": ([_vp, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                         _vp, _sz, _vp], _i32),
     "gumbel_verify": ([_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp], _i32),
+    "gumbel_topk": ([_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp], _i32),
     "biv_gumbel_workspace_bytes": ([_i32, _i32], _sz),
     "lm_head_gumbel_verify": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
     "kv_overwrite": ([_vp, _vp, _i64, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp], _i32),
@@ -222,6 +223,24 @@ def gumbel_verify(logits, noise, cand, target, accept_len, next_token):
     _check("gumbel_verify", _lib.gumbel_verify(_p(logits), _p(noise), _p(cand), R, K, V, _p(target),
                                                _p(accept_len), _p(next_token), _stream()))
     return target, accept_len, next_token
+
+
+def gumbel_topk(logits, noise, idx, score=None):
+    """idx [rows, k] int32 (and score [rows, k] fp32) <- the k largest
+    fl32(logit + noise) of each row of logits/noise [rows, V] fp32."""
+    _contig(logits, noise, idx)
+    _want(logits, torch.float32, "logits")
+    _want(noise, torch.float32, "noise")
+    _want(idx, torch.int32, "idx")
+    rows, k = idx.shape
+    V = logits.shape[-1]
+    assert logits.numel() == rows * V and noise.numel() == rows * V
+    if score is not None:
+        _contig(score)
+        _want(score, torch.float32, "score")
+        assert tuple(score.shape) == (rows, k)
+    _check("gumbel_topk", _lib.gumbel_topk(_p(logits), _p(noise), rows, V, k, _p(idx),
+                                           _p(score) if score is not None else None, _stream()))
 
 
 def gumbel_workspace_bytes(M, V):

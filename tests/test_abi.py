@@ -65,6 +65,10 @@ def test_host_side_argument_errors(lib):
     assert lib.gumbel_verify(None, None, None, 0, 4, 8, None, None, None, None) == 0  # R = 0
     lib.kv_overwrite.argtypes = [vp, vp, i64, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     assert lib.kv_overwrite(None, None, 4, None, None, None, 1, 8, 128, 10, 1, None) == 1  # stride < Hkv*D
+    lib.gumbel_topk.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
+    assert lib.gumbel_topk(bp, bp, 4, 100, 9, bp, None, None) == 2  # k > 8: unsupported
+    assert lib.gumbel_topk(bp, bp, 4, 5, 6, bp, None, None) == 1  # k > V
+    assert lib.gumbel_topk(None, None, 0, 100, 3, None, None, None) == 0  # no rows
     lib.lm_head_gumbel_verify.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.biv_gumbel_workspace_bytes.argtypes = [i32, i32]
     lib.biv_gumbel_workspace_bytes.restype = ctypes.c_size_t

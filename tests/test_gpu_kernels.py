@@ -135,6 +135,32 @@ def test_gumbel_verify_nan_inf_rows(biv):
     assert np.array_equal(acc.cpu().numpy(), a_ref) and np.array_equal(nxt.cpu().numpy(), n_ref)
 
 
+@pytest.mark.parametrize("rows,V,k", [(512, 128256, 8), (7, 1001, 3), (3, 5, 5), (40, 4096, 1)])
+def test_gumbel_topk_bitwise(biv, rows, V, k):
+    """Indices and scores bit for bit the oracle's, with planted exact ties, NaN
+    and -inf entries, and an all-NaN row; k = 1 equals gumbel_verify's target."""
+    l = wl.normal_f32(140 + V % 11, (rows, V), std=3.0)
+    g = wl.gumbel_noise(141, np.arange(rows), np.full(rows, 500), V)
+    if V > 20:
+        l[0, [3, 11, 17]] = np.float32(1e9)  # three-way exact tie
+        l[1, ::5] = np.nan
+        l[2 % rows, 1::2] = -np.inf
+    l[rows - 1, :] = np.nan
+    i_ref, s_ref = oracle.gumbel_topk(l, g, k)
+    idx = torch.full((rows, k), -3, dtype=torch.int32, device=DEV)
+    sc = torch.full((rows, k), 7.0, dtype=torch.float32, device=DEV)
+    announce("gumbel_topk", rows, V, k)
+    biv.gumbel_topk(dev_f32(l), dev_f32(g), idx, sc)
+    sync()
+    assert np.array_equal(idx.cpu().numpy(), i_ref)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), s_ref.astype(np.float32).view(np.uint32))
+    if V > 20:
+        assert list(i_ref[0, :min(k, 3)]) == [3, 11, 17][:min(k, 3)]
+    if k == 1:
+        t_ref, _, _ = oracle.gumbel_verify(l[:, None, :], g[:, None, :], np.zeros((rows, 1), np.int32))
+        assert np.array_equal(i_ref[:, 0], t_ref[:, 0])
+
+
 # =====================================================================
 # lm_head_gumbel_verify (lm_head matmul with the Gumbel argmax in its epilogue)
 # =====================================================================
