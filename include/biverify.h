@@ -144,12 +144,18 @@ biv_status gemm_bi(const void* A, const void* B, void* C, int64_t M, int64_t N, 
  * a one-workgroup launch before them that orders the segments.  The fp32 path
  * folds all chunk partials of a row in one ascending left fold (one launch).
  *
- * Supported: dt BIV_BF16 with D == 128 and q_len * (Hq/Hkv) <= 32 (bf16 MFMA
- * path); dt BIV_F32 with D in {64, 128} (fp32 path, any q_len).  Hq % Hkv == 0,
- * ctx[r] + q_len <= max_blocks * 16.
+ * Supported: dt BIV_BF16 with D == 128 and Hq/Hkv dividing 32 (bf16 MFMA
+ * path; any q_len: the rows of a request are taken 32/(Hq/Hkv) positions at a
+ * time, each such row block with its own keys 0 .. ctx[r] + its last
+ * position, so q_len up to a whole prompt gives a causal prefill whose rows
+ * are the same bits as decoding them one at a time); dt BIV_F32 with D in
+ * {64, 128} (fp32 path, any q_len).  Hq % Hkv == 0, ctx[r] + q_len <=
+ * max_blocks * 16, R * row blocks <= 65535.
  *
  * workspace: device memory of at least
- * biv_attn_workspace_bytes(R, Hkv, max_blocks, BIV_ATTN_SEG_TOKENS) bytes,
+ * biv_attn_workspace_bytes_q(R, q_len, Hq, Hkv, max_blocks, BIV_ATTN_SEG_TOKENS)
+ * bytes (equal to biv_attn_workspace_bytes(R, Hkv, max_blocks, ...) when
+ * q_len * Hq/Hkv <= 32),
  * 16-byte aligned (bf16 path; may be NULL for the fp32 path); it holds the
  * segment results between the two launches and, for grids of at least four
  * rounds of resident waves, the work list that launches the segments in
@@ -160,6 +166,8 @@ biv_status gemm_bi(const void* A, const void* B, void* C, int64_t M, int64_t N, 
 #define BIV_ATTN_SEG_TOKENS 2048
 
 size_t biv_attn_workspace_bytes(int R, int Hkv, int max_blocks, int seg_tokens);
+/* The same for any q_len: R requests of q_len rows (0 for unsupported shapes). */
+size_t biv_attn_workspace_bytes_q(int R, int q_len, int Hq, int Hkv, int max_blocks, int seg_tokens);
 
 biv_status attn_decode_bi(const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
                           const int32_t* block_table, const int32_t* ctx, void* out, int R, int q_len,

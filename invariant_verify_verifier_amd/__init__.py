@@ -6,6 +6,7 @@ that sequences those kernels (verifier).  There is no CPU or PyTorch
 fallback: importing fails if the library has not been built.
 """
 from ._lib import (  # noqa: F401
+    ATTN_SEG_TOKENS,
     SWIGLU_BLOCK,
     BivError,
     abi_version,

@@ -38,6 +38,7 @@ _SIGS = {
     "rmsnorm_bi": ([_vp, _i32, _vp, _vp, _i32, _i64, _i64, _f32, _vp], _i32),
     "gemm_bi": ([_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp], _i32),
     "biv_attn_workspace_bytes": ([_i32, _i32, _i32, _i32], _sz),
+    "biv_attn_workspace_bytes_q": ([_i32, _i32, _i32, _i32, _i32, _i32], _sz),
     "attn_decode_bi": ([_vp, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                         _vp, _sz, _vp], _i32),
     "gumbel_verify": ([_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp], _i32),
@@ -157,8 +158,12 @@ def pack_gate_up(w_gate_up):
     return w_gate_up.view(2, F // SWIGLU_BLOCK, SWIGLU_BLOCK, H).transpose(0, 1).contiguous().view(F2, H)
 
 
-def attn_workspace_bytes(R, Hkv, max_blocks, seg_tokens=ATTN_SEG_TOKENS):
-    return _lib.biv_attn_workspace_bytes(R, Hkv, max_blocks, seg_tokens)
+def attn_workspace_bytes(R, Hkv, max_blocks, seg_tokens=ATTN_SEG_TOKENS, q_len=1, Hq=None):
+    """Workspace of the bf16 attention for R requests of q_len rows (Hq query
+    heads; needed once q_len * Hq/Hkv > 32, i.e. several row blocks)."""
+    if Hq is None:
+        return _lib.biv_attn_workspace_bytes(R, Hkv, max_blocks, seg_tokens)
+    return _lib.biv_attn_workspace_bytes_q(R, q_len, Hq, Hkv, max_blocks, seg_tokens)
 
 
 def _attn_checks(q, k_cache, v_cache, block_table, ctx, out, q_len):

@@ -10,10 +10,12 @@
 // bf16 path.  The keys of a request are cut at fixed absolute positions:
 //   sub-tile = 32 keys (one MFMA block), chunk = 256 keys (the KV split),
 //   segment  = seg_tokens keys (2048 for the invariant kernel).
-// One 64-lane wave per (segment, KV head, request), four per CU.  The rows
-// of one KV head (q_len positions x G query heads <= 32) share one 32-row
-// MFMA block, so the K/V of a page is read once for all of them (the pages'
-// tile rule: G x (1+D) rows per KV head, here G x K <= 32).  The wave streams
+// One 64-lane wave per (segment, KV head, row block), four per CU.  The rows
+// of one KV head in a row block (32/G positions x G query heads) share one
+// 32-row MFMA block, so the K/V of a page is read once for all of them (the
+// pages' tile rule: G x (1+D) rows per KV head, here G x K <= 32: a verify
+// step of K <= 8 positions is one block per request; a longer q_len, e.g. a
+// prefill, takes several blocks, each with the keys up to its last row).  The wave streams
 // its segment's K and V sub-tiles from HBM straight into a ring of LDS slots
 // (gfx950 global_load_lds_dwordx4) and computes S^T = K Q^T and O^T = V^T P^T
 // on the 32x32x16 bf16 MFMA, softmax statistics in fp32 (log2 domain),
@@ -98,24 +100,27 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx,
     uint16_t* __restrict__ out, int q_len, int Hq, int Hkv, int max_blocks, int num_blocks, float scale_log2,
-    int seg_tokens, int nseg_max, AttnWs ws, const int32_t* __restrict__ items) {
+    int seg_tokens, int nseg_max, AttnWs ws, const int32_t* __restrict__ items, int blk_pos, int n_rb) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kRing * kSlot];
-  // grid: (segment, KV head, request), or with a work list a 1-D grid of
-  // (list entry, KV head), KV head fastest; an entry is r * nseg_max + seg
-  int seg, kvh, r;
+  // grid: (segment, KV head, row block), or with a work list a 1-D grid of
+  // (list entry, KV head), KV head fastest; an entry is v * nseg_max + seg.
+  // Row block v = r * n_rb + b holds query positions b*blk_pos .. +blk_pos-1
+  // of request r (one block, v = r, whenever q_len * G <= 32).
+  int seg, kvh, v;
   if (items != nullptr) {
     kvh = (int)(blockIdx.x % (unsigned)Hkv);
     const int e = items[blockIdx.x / (unsigned)Hkv];
     if (e < 0) return;
-    r = e / nseg_max;
-    seg = e - r * nseg_max;
+    v = e / nseg_max;
+    seg = e - v * nseg_max;
   } else {
     seg = blockIdx.x;
     kvh = blockIdx.y;
-    r = blockIdx.z;
+    v = blockIdx.z;
   }
+  const int r = v / n_rb, j0 = (v - r * n_rb) * blk_pos;  // request, first query position of the block
   const int lane = threadIdx.x, g = lane >> 5, li = lane & 31;
-  const int G = Hq / Hkv, nrows = q_len * G;
+  const int G = Hq / Hkv, jn = min(blk_pos, q_len - j0), nrows = jn * G;
   const int32_t* bt = block_table + (int64_t)r * max_blocks;
   const int page0 = seg * (seg_tokens >> 4);  // first page of the segment
 
@@ -128,7 +133,7 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
   if (seg_tokens > kPagesPerWin * 16 && page0 + kPagesPerWin + lane < max_blocks) bt_w1 = bt[page0 + kPagesPerWin + lane];
   // this lane's query row (MFMA column li)
   const bool row_ok = li < nrows;
-  const int jq = row_ok ? li / G : 0;
+  const int jq = j0 + (row_ok ? li / G : 0);
   const int hq = kvh * G + (row_ok ? li % G : 0);
   const int64_t qtok = (int64_t)r * q_len + jq;
   bf16x8 bq[8];
@@ -142,7 +147,7 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
     }
   }
 
-  const int n_tok = min(L + q_len, max_blocks * 16);
+  const int n_tok = min(L + j0 + jn, max_blocks * 16);  // keys of the block's last row
   const int nseg = (n_tok + seg_tokens - 1) / seg_tokens;
   if (seg >= nseg) return;
   const int tok_begin = seg * seg_tokens;  // a multiple of kChunk
@@ -385,7 +390,7 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
     return;
   }
   // segment result -> workspace; attn_combine_kernel folds the segments
-  const int64_t slot = ((int64_t)r * Hkv + kvh) * nseg_max + seg;
+  const int64_t slot = ((int64_t)v * Hkv + kvh) * nseg_max + seg;
   float* slot_o = ws.part_o + slot * 4096;
 #pragma unroll
   for (int qg = 0; qg < 16; ++qg) {  // one 1 KiB streaming store per group of four values
@@ -402,9 +407,9 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
 // the work changes: each item's arithmetic and its workspace slot are fixed
 // by (request, segment), so the results are the same bits.  One workgroup;
 // partial lengths are bucketed in 128 classes.
-__global__ __launch_bounds__(1024) void attn_plan_kernel(const int32_t* __restrict__ ctx, int R, int q_len,
-                                                        int max_blocks, int seg_tokens, int nseg_max,
-                                                        int32_t* __restrict__ items) {
+__global__ __launch_bounds__(1024) void attn_plan_kernel(const int32_t* __restrict__ ctx, int Rv, int q_len,
+                                                        int max_blocks, int seg_tokens, int nseg_max, int blk_pos,
+                                                        int n_rb, int32_t* __restrict__ items) {
   constexpr int NB = 128;
   __shared__ int n_full, full_cur, bucket_cnt[NB], bucket_start[NB], bucket_cur[NB];
   const int tid = threadIdx.x;
@@ -419,8 +424,13 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(const int32_t* __restri
   __syncthreads();
   const int cap = max_blocks * 16;
   const int bw = (seg_tokens + NB - 1) / NB;
-  for (int r = tid; r < R; r += 1024) {
-    const int nt = min(ctx[r] + q_len, cap);
+  // keys of row block v: up to the block's last query position
+  auto block_tokens = [&](int v) {
+    const int r = v / n_rb, j0 = (v - r * n_rb) * blk_pos;
+    return min(ctx[r] + j0 + min(blk_pos, q_len - j0), cap);
+  };
+  for (int v = tid; v < Rv; v += 1024) {
+    const int nt = block_tokens(v);
     const int full = nt / seg_tokens, part = nt - full * seg_tokens;
     atomicAdd(&n_full, full);
     if (part > 0) atomicAdd(&bucket_cnt[(part - 1) / bw], 1);
@@ -434,18 +444,18 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(const int32_t* __restri
     }
   }
   __syncthreads();
-  for (int r = tid; r < R; r += 1024) {
-    const int nt = min(ctx[r] + q_len, cap);
+  for (int v = tid; v < Rv; v += 1024) {
+    const int nt = block_tokens(v);
     const int full = nt / seg_tokens, part = nt - full * seg_tokens;
     const int base = atomicAdd(&full_cur, full);
-    for (int k = 0; k < full; ++k) items[base + k] = r * nseg_max + k;
+    for (int k = 0; k < full; ++k) items[base + k] = v * nseg_max + k;
     if (part > 0) {
       const int b = (part - 1) / bw;
-      items[bucket_start[b] + atomicAdd(&bucket_cur[b], 1)] = r * nseg_max + full;
+      items[bucket_start[b] + atomicAdd(&bucket_cur[b], 1)] = v * nseg_max + full;
     }
   }
   const int n_items = bucket_start[0] + bucket_cnt[0];
-  for (int i = n_items + tid; i < R * nseg_max; i += 1024) items[i] = -1;
+  for (int i = n_items + tid; i < Rv * nseg_max; i += 1024) items[i] = -1;
 }
 
 // Waves of the segment kernel resident at once on the current device (four
@@ -473,15 +483,16 @@ constexpr int kCombThreads = 1024, kCombBatch = 8;
 __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(const int32_t* __restrict__ ctx,
                                                                     uint16_t* __restrict__ out, int q_len, int Hq,
                                                                     int Hkv, int max_blocks, int seg_tokens,
-                                                                    int nseg_max, AttnWs ws) {
-  const int kvh = blockIdx.x, r = blockIdx.y;
+                                                                    int nseg_max, AttnWs ws, int blk_pos, int n_rb) {
+  const int kvh = blockIdx.x, v = blockIdx.y;  // v: row block, as in the first pass
+  const int r = v / n_rb, j0 = (v - r * n_rb) * blk_pos;
   const int tid = threadIdx.x, q = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
-  const int G = Hq / Hkv, nrows = q_len * G;
-  const int n_tok = min(ctx[r] + q_len, max_blocks * 16);
+  const int G = Hq / Hkv, jn = min(blk_pos, q_len - j0), nrows = jn * G;
+  const int n_tok = min(ctx[r] + j0 + jn, max_blocks * 16);
   const int nseg = (n_tok + seg_tokens - 1) / seg_tokens;
   if (nseg <= 1 || li >= nrows) return;  // single segment: written by the first pass
-  const int jq = li / G, hq = kvh * G + li % G;
-  const int64_t slot0 = ((int64_t)r * Hkv + kvh) * nseg_max;
+  const int jq = j0 + li / G, hq = kvh * G + li % G;
+  const int64_t slot0 = ((int64_t)v * Hkv + kvh) * nseg_max;
   float M = -INFINITY, Lt = 0.0f, O[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int s0 = 0; s0 < nseg; s0 += kCombBatch) {
     float o[kCombBatch][4], m[kCombBatch], l[kCombBatch];
@@ -600,14 +611,23 @@ static biv_status check_attn(const char* who, const void* q, int64_t q_stride, c
   return BIV_OK;
 }
 
+// Query positions per 32-row block (G query heads per KV head share a block)
+// and the number of blocks a request's q_len rows take.
+static inline int attn_blk_pos(int Hq, int Hkv) { return 32 / (Hq / Hkv); }
+static inline int attn_row_blocks(int q_len, int Hq, int Hkv) { return (int)cdiv(q_len, attn_blk_pos(Hq, Hkv)); }
+
 static biv_status launch_attn_bf16(const char* who, const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
                                    const int32_t* block_table, const int32_t* ctx, void* out, int R, int q_len,
                                    int Hq, int Hkv, int max_blocks, int num_blocks, float scale, int seg_tokens,
                                    void* workspace, size_t workspace_bytes, hipStream_t s) {
-  BIV_REQUIRE(q_len * (Hq / Hkv) <= 32, "%s: bf16 path needs q_len*Hq/Hkv <= 32 (got %d)", who, q_len * (Hq / Hkv));
+  const int G = Hq / Hkv;
+  BIV_REQUIRE(G >= 1 && 32 % G == 0, "%s: bf16 path needs Hq/Hkv dividing 32 (got %d)", who, G);
+  const int blk_pos = attn_blk_pos(Hq, Hkv), n_rb = attn_row_blocks(q_len, Hq, Hkv);
+  BIV_REQUIRE((int64_t)R * n_rb <= 65535, "%s: %d requests x %d row blocks exceed the grid", who, R, n_rb);
+  const int Rv = R * n_rb;  // row blocks
   BIV_REQUIRE(aligned16(q) && aligned16(k_cache) && aligned16(v_cache) && q_stride % 8 == 0,
               "%s: q (and its row stride) and the caches must be 16-byte aligned", who);
-  const size_t need = biv_attn_workspace_bytes(R, Hkv, max_blocks, seg_tokens);
+  const size_t need = biv_attn_workspace_bytes(Rv, Hkv, max_blocks, seg_tokens);
   BIV_REQUIRE(workspace != nullptr && workspace_bytes >= need, "%s: workspace needs %zu bytes (got %zu)", who, need,
               workspace_bytes);
   BIV_REQUIRE(aligned16(workspace), "%s: workspace must be 16-byte aligned", who);
@@ -615,16 +635,16 @@ static biv_status launch_attn_bf16(const char* who, const void* q, int64_t q_str
   BIV_REQUIRE(nseg_max <= 0x7fffffff, "%s: too many segments", who);
   AttnWs ws;
   ws.part_o = static_cast<float*>(workspace);
-  ws.part_ml = ws.part_o + (size_t)R * Hkv * nseg_max * 4096;
+  ws.part_ml = ws.part_o + (size_t)Rv * Hkv * nseg_max * 4096;
   // A grid of at least four rounds of resident waves is launched in LPT
   // order from a work list (decided by the call's shape alone).
-  const int64_t waves = (int64_t)R * nseg_max * Hkv;
+  const int64_t waves = (int64_t)Rv * nseg_max * Hkv;
   int32_t* items = nullptr;
-  dim3 grid(nseg_max, Hkv, R);
+  dim3 grid(nseg_max, Hkv, Rv);
   if (waves >= 4 * (int64_t)resident_attn_waves() && waves <= 0x7fffffff) {
-    items = reinterpret_cast<int32_t*>(ws.part_ml + (size_t)R * Hkv * nseg_max * 128);
-    hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, s, ctx, R, q_len, max_blocks, seg_tokens, nseg_max,
-                       items);
+    items = reinterpret_cast<int32_t*>(ws.part_ml + (size_t)Rv * Hkv * nseg_max * 128);
+    hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, s, ctx, Rv, q_len, max_blocks, seg_tokens, nseg_max,
+                       blk_pos, n_rb, items);
     biv_status st = launched(who);
     if (st != BIV_OK) return st;
     grid = dim3((unsigned)waves);
@@ -632,11 +652,11 @@ static biv_status launch_attn_bf16(const char* who, const void* q, int64_t q_str
   hipLaunchKernelGGL(attn_bf16_kernel, grid, dim3(64), 0, s, static_cast<const uint16_t*>(q), q_stride,
                      static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache), block_table, ctx,
                      static_cast<uint16_t*>(out), q_len, Hq, Hkv, max_blocks, num_blocks, scale * kLog2e,
-                     seg_tokens, nseg_max, ws, items);
+                     seg_tokens, nseg_max, ws, items, blk_pos, n_rb);
   biv_status st = launched(who);
   if (st != BIV_OK || nseg_max <= 1) return st;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(Hkv, R), dim3(kCombThreads), 0, s, ctx, static_cast<uint16_t*>(out), q_len,
-                     Hq, Hkv, max_blocks, seg_tokens, nseg_max, ws);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(Hkv, Rv), dim3(kCombThreads), 0, s, ctx, static_cast<uint16_t*>(out),
+                     q_len, Hq, Hkv, max_blocks, seg_tokens, nseg_max, ws, blk_pos, n_rb);
   return launched(who);
 }
 
@@ -648,6 +668,14 @@ extern "C" size_t biv_attn_workspace_bytes(int R, int Hkv, int max_blocks, int s
   const size_t nseg = (size_t)cdiv((int64_t)max_blocks * 16, seg_tokens);
   // segment results, then the work list of large grids (R * nseg entries)
   return (size_t)R * Hkv * nseg * (4096 + 128) * sizeof(float) + (size_t)R * nseg * sizeof(int32_t);
+}
+
+extern "C" size_t biv_attn_workspace_bytes_q(int R, int q_len, int Hq, int Hkv, int max_blocks, int seg_tokens) {
+  using namespace biv;
+  if (R <= 0 || q_len <= 0 || Hkv <= 0 || Hq < Hkv || Hq % Hkv != 0 || 32 % (Hq / Hkv) != 0) return 0;
+  const int64_t rv = (int64_t)R * attn_row_blocks(q_len, Hq, Hkv);
+  if (rv > 0x7fffffff) return 0;
+  return biv_attn_workspace_bytes((int)rv, Hkv, max_blocks, seg_tokens);
 }
 
 extern "C" biv_status attn_decode_bi(const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
@@ -663,8 +691,8 @@ extern "C" biv_status attn_decode_bi(const void* q, int64_t q_stride, const void
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dt == BIV_BF16) {
     if (D != kHD) return fail(BIV_EUNSUPPORTED, "attn_decode_bi: bf16 path supports D == 128 only (D=%d)", D);
-    if (q_len * (Hq / Hkv) > 32)
-      return fail(BIV_EUNSUPPORTED, "attn_decode_bi: bf16 path needs q_len*Hq/Hkv <= 32 (got %d)", q_len * (Hq / Hkv));
+    if (32 % (Hq / Hkv) != 0)
+      return fail(BIV_EUNSUPPORTED, "attn_decode_bi: bf16 path needs Hq/Hkv dividing 32 (got %d)", Hq / Hkv);
     return launch_attn_bf16("attn_decode_bi", q, q_stride, k_cache, v_cache, block_table, ctx, out, R, q_len, Hq, Hkv,
                             max_blocks, num_blocks, scale, BIV_ATTN_SEG_TOKENS, workspace, workspace_bytes, s);
   }
@@ -695,7 +723,7 @@ extern "C" biv_status attn_decode_adaptive(const void* q, int64_t q_stride, cons
   if (st != BIV_OK) return st;
   if (R == 0) return BIV_OK;
   if (D != kHD) return fail(BIV_EUNSUPPORTED, "attn_decode_adaptive: supports D == 128 only (D=%d)", D);
-  if (q_len * (Hq / Hkv) > 32) return fail(BIV_EUNSUPPORTED, "attn_decode_adaptive: needs q_len*Hq/Hkv <= 32");
+  if (32 % (Hq / Hkv) != 0) return fail(BIV_EUNSUPPORTED, "attn_decode_adaptive: needs Hq/Hkv dividing 32");
   BIV_REQUIRE(split_tokens >= 0 && split_tokens % kChunk == 0, "attn_decode_adaptive: split_tokens must be a multiple of %d", kChunk);
   const int split = split_tokens == 0 ? biv_attn_adaptive_split(R, Hkv, max_blocks) : split_tokens;
   return launch_attn_bf16("attn_decode_adaptive", q, q_stride, k_cache, v_cache, block_table, ctx, out, R, q_len, Hq, Hkv,

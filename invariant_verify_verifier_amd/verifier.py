@@ -132,11 +132,11 @@ class VerifierModel:
             self._bufs[W] = b
         return b
 
-    def workspace(self, R, max_blocks):
-        key = (R, max_blocks)
+    def workspace(self, R, max_blocks, q_len=1):
+        key = (R, max_blocks, q_len)
         ws = self._ws.get(key)
         if ws is None:
-            nbytes = L.attn_workspace_bytes(R, self.shape.kv_heads, max_blocks)
+            nbytes = L.attn_workspace_bytes(R, self.shape.kv_heads, max_blocks, q_len=q_len, Hq=self.shape.heads)
             ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=self.device)
             self._ws[key] = ws
         return ws
@@ -152,7 +152,7 @@ class VerifierModel:
         R, mb = block_table.shape
         b = self._buffers(W)
         x, h, qkv, attn, gu, act, logits = b["x"], b["h"], b["qkv"], b["attn"], b["gu"], b["act"], b["logits"]
-        ws = self.workspace(R, mb) if self.dtype == torch.bfloat16 else None
+        ws = self.workspace(R, mb, q_len) if self.dtype == torch.bfloat16 else None
         scale = 1.0 / math.sqrt(sh.head_dim)
         gemm = gemm_fn or L.gemm_bi
         attend = attn_fn or L.attn_decode_bi

@@ -90,11 +90,21 @@ def test_host_side_argument_errors(lib):
     # Hq not a multiple of Hkv
     assert lib.attn_decode_bi(None, 4096, None, None, None, None, None, 1, 1, 30, 8, 128, 4, 4, 0.1, 1, None, 0,
                               None) == 1
-    # bf16 path with too many rows per KV head (q_len * G > 32) is unsupported, not invalid
+    # bf16 path: G = Hq/Hkv must divide 32 (unsupported otherwise, not invalid); q_len * G > 32 takes
+    # several row blocks and a workspace sized for them
     buf = ctypes.create_string_buffer(64)
     p = ctypes.cast(buf, vp)
-    st = lib.attn_decode_bi(p, 4096, p, p, p, p, p, 1, 16, 32, 8, 128, 4, 4, 0.1, 1, p, 64, None)
-    assert st == 2
+    assert lib.attn_decode_bi(p, 4096, p, p, p, p, p, 1, 16, 24, 8, 128, 4, 4, 0.1, 1, p, 64, None) == 2
+    assert lib.attn_decode_bi(p, 4096, p, p, p, p, p, 1, 16, 32, 8, 128, 4, 4, 0.1, 1, p, 64, None) == 1
+    assert b"workspace" in lib.biv_last_error()
+    lib.biv_attn_workspace_bytes_q.restype = ctypes.c_size_t
+    lib.biv_attn_workspace_bytes_q.argtypes = [ctypes.c_int] * 6
+    lib.biv_attn_workspace_bytes.restype = ctypes.c_size_t
+    lib.biv_attn_workspace_bytes.argtypes = [ctypes.c_int] * 4
+    # 200 rows, G = 4: 25 row blocks of 8 positions
+    assert lib.biv_attn_workspace_bytes_q(3, 200, 32, 8, 40, 2048) == lib.biv_attn_workspace_bytes(75, 8, 40, 2048)
+    assert lib.biv_attn_workspace_bytes_q(3, 8, 32, 8, 40, 2048) == lib.biv_attn_workspace_bytes(3, 8, 40, 2048)
+    assert lib.biv_attn_workspace_bytes_q(3, 8, 24, 8, 40, 2048) == 0
 
 
 def test_workspace_sizes(lib):

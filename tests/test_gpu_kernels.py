@@ -602,8 +602,8 @@ def _run_attn(biv, lay, kc, vc, q, q_len, dtype="bf16", fn=None, **kw):
     ws = None
     if dtype == "bf16":
         seg = kw.pop("seg", None)
-        nbytes = (biv.attn_workspace_bytes(len(lay.ctx), kc.shape[1], lay.max_blocks) if seg is None
-                  else biv.attn_workspace_bytes(len(lay.ctx), kc.shape[1], lay.max_blocks, seg))
+        nbytes = biv.attn_workspace_bytes(len(lay.ctx), kc.shape[1], lay.max_blocks,
+                                          seg if seg is not None else biv.ATTN_SEG_TOKENS, q_len=q_len, Hq=Hq)
         ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
     (fn or biv.attn_decode_bi)(dev(q), kcd, vcd, bt, cx, out, q_len, 1.0 / math.sqrt(D), ws, **kw)
     sync()
@@ -676,6 +676,31 @@ def test_attention_bf16_verify_rows_equal_single_decodes(biv):
                               num_blocks=lay.num_blocks, max_blocks=lay.max_blocks)
         one = bits(_run_attn(biv, lay1, kc, vc, q[j:j + 1], 1))
         assert np.array_equal(one[0], block[j]), f"row {j}"
+
+
+@pytest.mark.parametrize("q_len,G", [(33, 4), (200, 4), (70, 1)])
+def test_attention_bf16_row_blocks_prefill(biv, q_len, G):
+    """q_len beyond one 32-row block (a prefill, or a long verify): the rows
+    are taken 32/G positions at a time, each block with the keys up to its own
+    last row.  Parity with the oracle (contexts 0 -- a causal prefill -- and
+    across chunk and segment boundaries), and sampled rows bit for bit those of
+    single-row decodes at context L + j."""
+    Hkv = 8 if G == 4 else 4
+    Hq = Hkv * G
+    ctx = [0, 700, 2300]
+    R = len(ctx)
+    lay, kc, vc, q = _attn_inputs(R, q_len, Hq, Hkv, 128, ctx, seed=150 + q_len + G)
+    announce("attention bf16 row blocks", q_len, G)
+    out = _run_attn(biv, lay, kc, vc, q, q_len)
+    check_bf16(f64(out), _attn_ref(lay, kc, vc, q, q_len), f"attention bf16 q_len={q_len} G={G}")
+    full = bits(out)
+    blk = 32 // G
+    for r in range(R):
+        for j in sorted({0, blk - 1, blk, q_len // 2, q_len - 1}):
+            lay1 = wl.PagedLayout(ctx=np.array([ctx[r] + j], np.int32), q_len=1, block_table=lay.block_table[r:r + 1],
+                                  num_blocks=lay.num_blocks, max_blocks=lay.max_blocks)
+            one = bits(_run_attn(biv, lay1, kc, vc, q[r * q_len + j:r * q_len + j + 1], 1))
+            assert np.array_equal(one[0], full[r * q_len + j]), f"request {r} row {j}"
 
 
 def test_attention_f32_parity(biv):
