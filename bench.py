@@ -48,6 +48,11 @@ def parse():
                    help="instead of the pass: decode-verify-rollback at the pass's shape (split-K fast path, K=8, "
                         "--rounds rounds) against one-token-at-a-time invariant decoding and the fast path alone")
     p.add_argument("--rounds", type=int, default=3, help="verification rounds in --dvr")
+    p.add_argument("--prefill", action="store_true",
+                   help="instead of the pass: causal prefill of --prompts prompts of --prompt-len tokens at the 8B "
+                        "shape with the batch-invariant kernels (one forward, q_len = prompt length)")
+    p.add_argument("--prompts", type=int, default=4)
+    p.add_argument("--prompt-len", type=int, default=2048)
     p.add_argument("--attn-only", action="store_true",
                    help="only the pass's attention call (same contexts, pages and shapes) and a 512 MiB copy, "
                         "--iters times each: the program the HBM traffic counters are collected on")
@@ -481,6 +486,62 @@ def micro(args):
         torch.cuda.empty_cache()
 
 
+def prefill_bench(args):
+    """Causal prefill with the batch-invariant kernels at the 8B shape: R
+    prompts of P tokens from context 0 in one forward (q_len = P; attention
+    in 32-row blocks, each with the keys up to its own last row), writing the
+    prompts' K/V.  Its rows are bit for bit those of decoding the prompt one
+    token at a time (tested on the 2-layer slice)."""
+    import torch
+
+    import workloads as wl
+    from invariant_verify_verifier_amd import verifier as V
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    sh, R, P = wl.LLAMA3_8B, args.prompts, args.prompt_len
+    print(f"[bench] prefill setup: {args.layers} layers, {R} prompts x {P} tokens", file=sys.stderr, flush=True)
+    dw = wl.device_model_weights(sh, wl.SEEDS["pass_weights"], layers=args.layers)
+    shape = V.Shape(args.layers, sh.hidden, sh.heads, sh.kv_heads, sh.head_dim, sh.ffn, sh.vocab, sh.eps,
+                    sh.rope_theta)
+    model = V.VerifierModel(shape, torch.bfloat16, dw["layers"], dw["embed"], dw["lm_head"], dw["final_norm"],
+                            max_pos=max(16384, P + 16))
+    ctx = np.zeros(R, np.int32)
+    lay = wl.paged_layout(ctx, P, seed=wl.SEEDS["pass_len"] + 3)
+    caches = model.alloc_kv(lay.num_blocks)
+    pos = np.tile(np.arange(P, dtype=np.int32), R)
+    rows = np.repeat(np.arange(R), P)
+    slots = lay.block_table[rows, pos // 16].astype(np.int64) * 16 + pos % 16
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    toks, pos_d, ctx_d, bt, sl = (dev(wl.tokens(wl.SEEDS["pass_tokens"] + 5, (R * P,), sh.vocab)), dev(pos),
+                                  dev(ctx), dev(lay.block_table), dev(slots))
+    run = lambda: model.forward(toks, pos_d, ctx_d, P, bt, sl, caches)
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        run()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    # the lm_head over every prompt row is part of this forward (logits of all rows)
+    flops = 2.0 * R * P * (args.layers * (sh.hidden * (sh.heads + 2 * sh.kv_heads) * sh.head_dim
+                                          + sh.heads * sh.head_dim * sh.hidden + 3 * sh.hidden * sh.ffn)
+                           + sh.hidden * sh.vocab)
+    attn_flops = 4.0 * args.layers * R * sh.heads * sh.head_dim * (P * (P + 1) / 2)
+    line = {"metric": "prefill tokens/s (1 GPU)", "value": round(R * P / (ms / 1e3), 1), "unit": "prompt tok/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
+            "higher_is_better": True, "dtype": "bf16",
+            "data": "synthetic (seeded random-init weights, random prompt tokens)",
+            "config": {"workload": f"Llama-3-8B-shaped causal prefill ({args.layers} layers), {R} prompts x {P} tokens "
+                                   "from context 0, batch-invariant kernels, logits of every row",
+                       "prompts": R, "prompt_len": P},
+            "mfma_tflops": round((flops + attn_flops) / (ms / 1e3) / 1e12, 1)}
+    print(json.dumps(line), flush=True)
+
+
 def dvr_bench(args):
     """Decode-verify-rollback (LLM-42 post, paragraphs 3-4) at the pass's
     shape: N = 64 requests, K = 8, contexts U[2048, 8192].  Three ways to
@@ -582,6 +643,9 @@ def main():
     args = parse()
     if args.micro and args.gpus == 1:
         micro(args)
+        return
+    if args.prefill and args.gpus == 1:
+        prefill_bench(args)
         return
     if args.dvr and args.gpus == 1:
         dvr_bench(args)
