@@ -132,3 +132,22 @@ def test_rope_table_host_values(lib):
         a = 3 * 100.0 ** (-2 * i / D)
         assert abs(buf[(3 * D // 2 + i) * 2] - math.cos(a)) < 1e-7
         assert abs(buf[(3 * D // 2 + i) * 2 + 1] - math.sin(a)) < 1e-7
+
+
+def test_dvr_round_stats_and_rollback_rule():
+    """Host bookkeeping of decode-verify-rollback (LLM-42 post, paragraph 3):
+    acceptance is the accepted share of drafted tokens, tokens per round the
+    committed count (prefix plus correction, all K when nothing diverges)."""
+    import numpy as np
+
+    from invariant_verify_verifier_amd import dvr, verifier
+
+    st = dvr.RoundStats()
+    assert np.isnan(st.acceptance(8)) and np.isnan(st.tokens_per_round())
+    cand = np.array([[5, 6, 7, 8], [5, 6, 7, 8], [5, 6, 7, 8]])
+    acc = np.array([0, 2, 4])
+    new_ctx, committed, t0 = verifier.rollback(np.array([10, 20, 30]), acc, np.array([9, 9, -1]), cand)
+    assert list(new_ctx) == [11, 23, 34] and committed == [[9], [5, 6, 9], [5, 6, 7, 8]] and list(t0) == [9, 9, 8]
+    st.accept_len.append(acc)
+    st.committed.append(np.array([len(c) for c in committed]))
+    assert st.acceptance(4) == 0.5 and abs(st.tokens_per_round() - 8 / 3) < 1e-12
