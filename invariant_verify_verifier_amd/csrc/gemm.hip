@@ -13,8 +13,8 @@
 // it lands in, not on the other rows.  The tiling depends on the weight shape
 // alone and is the same for every M.
 //  - gemm_dma_kernel (K a multiple of 64, the decoder's case): A and B tiles
-//    copied HBM -> LDS by global_load_lds_dwordx4 into a ring of 64-wide k
-//    stages; tile shape and wave arrangement chosen per weight width (see
+//    copied HBM -> LDS by global_load_lds_dwordx4 into a ring of 64- or
+//    128-wide k stages; tile shape and wave arrangement chosen per weight width (see
 //    dma_tile_for); store, residual-accumulate and SwiGLU epilogues.
 //  - gemm_bf16_kernel (any K % 8 == 0): 128 x 128 tiles, K staged 64 at a time
 //    through registers into double-buffered, XOR-swizzled LDS; four waves of
@@ -149,20 +149,25 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(const uint16_t*
 // The same per-element reduction as gemm_bf16_kernel -- one 32x32x16 MFMA
 // shape, k ascending in steps of 16, lanes 0-31 holding k 0..7 and lanes 32-63
 // k 8..15 of each step -- so the two kernels give identical bits, and a row's
-// bits never depend on M or on the tile it lands in.  K advances 64 per stage;
-// each stage's A (BM x 64) and B (BN x 64) tiles are copied HBM -> LDS by
-// global_load_lds_dwordx4 in 1 KiB windows of 8 rows x 128 B (whole 128-byte
-// lines: half-line rows move at roughly half the rate), STAGES - 1 stages in
-// flight ahead of the one being multiplied.  WAVES_M x WAVES_N waves own
-// (BM/WAVES_M) x (BN/WAVES_N) outputs each.  The tile shape is chosen from
-// the weight shape (N) alone.
+// bits never depend on M or on the tile it lands in.  K advances KB (64 or
+// 128) per stage; each stage's A (BM x KB) and B (BN x KB) tiles are copied
+// HBM -> LDS by global_load_lds_dwordx4 in 1 KiB windows of 8 rows x 128 B or
+// 4 rows x 256 B (whole 128-byte lines: half-line rows move at roughly half
+// the rate), STAGES - 1 stages in flight ahead of the one being multiplied.
+// WAVES_M x WAVES_N waves own (BM/WAVES_M) x (BN/WAVES_N) outputs each.  The
+// tile shape is chosen from the weight shape (N) alone, its k width from K.
 constexpr int kDBK = 64;
 
-// 16-byte chunk c of LDS row r (128 B) is stored at position c ^ gemm_swz(r):
-// any 16 consecutive rows read at one logical chunk land in 16 distinct
-// 16-byte slots of the 256-byte span they share two by two, so a ds_read_b128
-// of 32 rows is bank-conflict free.
-__device__ __forceinline__ int gemm_swz(int r) { return (r >> 1) & 7; }
+// 16-byte chunk c of LDS row r is stored at position c ^ gemm_swz<KB>(r).
+// 128-byte rows (KB = 64): any 16 consecutive rows read at one logical chunk
+// land in 16 distinct 16-byte slots of the 256-byte span they share two by
+// two.  256-byte rows (KB = 128): each row spans all 64 banks, and 16
+// consecutive rows put one logical chunk in 16 distinct slots.  Either way a
+// ds_read_b128 of 32 rows is bank-conflict free.
+template <int KB>
+__device__ __forceinline__ int gemm_swz(int r) {
+  return KB == 64 ? ((r >> 1) & 7) : (r & 15);
+}
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding)
 template <int kN>
@@ -201,15 +206,18 @@ __device__ __forceinline__ void gumbel_fold_step(float* bv, int* bi, int li) {
   }
 }
 
-template <int BM, int BN, int STAGES, int WAVES_M, int WAVES_N, int OUT_DT, int EPI, bool kSplit>
+template <int BM, int BN, int STAGES, int WAVES_M, int WAVES_N, int OUT_DT, int EPI, bool kSplit, int KB>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_kernel(const uint16_t* __restrict__ A,
                                                        const uint16_t* __restrict__ B, void* C,
                                                        float* __restrict__ partial, int M, int N, int K,
                                                        int tilesM, int tilesN, int k_per_split) {
-  constexpr int ROW = kDBK * 2;  // 128 bytes of K per row per stage
+  static_assert(KB == 64 || KB == 128, "k width per stage");
+  constexpr int ROW = KB * 2;     // bytes of K per row per stage: 128 or 256
+  constexpr int RPW = 1024 / ROW;  // rows per 1 KiB copy window: 8 or 4
+  constexpr int CPR = ROW / 16;    // 16-byte chunks per row: 8 or 16
   constexpr int A_BYTES = BM * ROW;
   constexpr int STAGE = (BM + BN) * ROW;
-  constexpr int WIN = (BM + BN) / 8;  // 1 KiB windows per stage
+  constexpr int WIN = (BM + BN) / RPW;  // 1 KiB windows per stage
   constexpr int NW = WAVES_M * WAVES_N;
   static_assert(WIN % NW == 0, "windows must split evenly over the waves");
   constexpr int PER_WAVE = WIN / NW;
@@ -225,24 +233,24 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_kernel(const 
   const int n0 = (logical / tilesM) * BN;
   const int k_begin = kSplit ? blockIdx.y * k_per_split : 0;
   const int k_end = kSplit ? min(K, k_begin + k_per_split) : K;
-  const int nk = (k_end - k_begin) / kDBK;
+  const int nk = (k_end - k_begin) / KB;
 
   // This wave's DMA windows: j = wave + NW q, A windows first, then B.  Window
-  // j holds rows 8j..8j+7 of its operand; lane -> row lane/8 of the window,
-  // LDS chunk lane%8 holding logical chunk (lane%8) ^ gemm_swz(8j + lane/8),
-  // which depends on j only through its parity (wave and q fix it).
-  const int r_in = lane >> 3;
+  // j holds rows RPW j .. RPW j + RPW - 1 of its operand; lane -> row
+  // lane / CPR of the window, LDS chunk lane % CPR holding logical chunk
+  // (lane % CPR) ^ gemm_swz(RPW j + lane / CPR).
+  const int r_in = lane / CPR;
   const unsigned char* gbase[PER_WAVE];
   unsigned voff[PER_WAVE];
 #pragma unroll
   for (int q = 0; q < PER_WAVE; ++q) {
     const int j = wave + NW * q;
-    const bool isA = j < BM / 8;
-    const int row0 = isA ? m0 + 8 * j : n0 + 8 * (j - BM / 8);
+    const bool isA = j < BM / RPW;
+    const int row0 = isA ? m0 + RPW * j : n0 + RPW * (j - BM / RPW);
     const int rows = isA ? M : N;
     const int first = min(row0, rows - 1);       // window base row, in range
     const int row = min(row0 + r_in, rows - 1);  // rows past the edge re-read the last row
-    const int c_log = (lane & 7) ^ gemm_swz(8 * j + r_in);
+    const int c_log = (lane % CPR) ^ gemm_swz<KB>(RPW * j + r_in);
     const uint16_t* src = isA ? A : B;
     gbase[q] = reinterpret_cast<const unsigned char*>(src + (int64_t)first * K + k_begin);
     voff[q] = (unsigned)((row - first) * K * 2 + c_log * 16);
@@ -255,10 +263,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_kernel(const 
   };
 
   // fragment offsets: row li of a 32-row block, logical chunk 2 ks + g
-  const int xs = gemm_swz(li);
-  int off[kDBK / 16];
+  const int xs = gemm_swz<KB>(li);
+  int off[KB / 16];
 #pragma unroll
-  for (int ks = 0; ks < kDBK / 16; ++ks) off[ks] = li * ROW + 16 * ((2 * ks + g) ^ xs);
+  for (int ks = 0; ks < KB / 16; ++ks) off[ks] = li * ROW + 16 * ((2 * ks + g) ^ xs);
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -282,7 +290,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_kernel(const 
     // hides it).  Small wave tiles read the whole stage up front; large ones
     // read step ks + 1 while step ks multiplies.  The sched_barrier keeps the
     // compiler from sinking the reads back next to their uses.
-    constexpr int KS = kDBK / 16;
+    constexpr int KS = KB / 16;
     constexpr bool kWhole = (FM + FN) <= 3;
     constexpr int NBUF = kWhole ? KS : 2;
     bf16x8 a[NBUF][FM], b[NBUF][FN];
@@ -507,11 +515,15 @@ enum DmaTile { kTileL = 0, kTileS = 1, kTileQ = 2, kTileT = 3 };
 #define BIV_GEMM_S_TILE 128, 64, 3, 4, 2
 #endif
 #ifndef BIV_GEMM_Q_TILE
-#define BIV_GEMM_Q_TILE 128, 96, 4, 4, 1
+#define BIV_GEMM_Q_TILE 128, 96, 2, 4, 1  // 128-wide k stages (K % 128 == 0)
+#endif
+#ifndef BIV_GEMM_Q64_TILE
+#define BIV_GEMM_Q64_TILE 128, 96, 4, 4, 1  // the same tile with 64-wide k stages
 #endif
 #ifndef BIV_GEMM_T_TILE
 #define BIV_GEMM_T_TILE 128, 64, 4, 4, 2
 #endif
+
 // Columns per wave of a tile: the group width of the Gumbel epilogue's
 // per-row partial results (lm_head_gumbel_verify runs the L tile).
 template <int BM, int BN, int STAGES, int WAVES_M, int WAVES_N>
@@ -523,15 +535,15 @@ constexpr int kGumbelGroup = wave_cols<BIV_GEMM_L_TILE>();
 static DmaTile dma_tile_for(int64_t N) {
   if (N >= 16384) return kTileL;  // 256 x 256, 8 waves of 128 x 64, 2 stages (128 KiB LDS)
   if (N >= 8192) return kTileS;   // 128 x 64, 8 waves of 32 x 32, 3 stages (72 KiB)
-  if (N > 4096) return kTileQ;    // 128 x 96, 4 waves of 32 x 96, 4 stages (112 KiB)
+  if (N > 4096) return kTileQ;    // 128 x 96, 4 waves of 32 x 96, 2 stages of 128-wide k (112 KiB)
   return kTileT;                  // 128 x 64, 8 waves of 32 x 32, 4 stages (96 KiB)
 }
 
-template <int BM, int BN, int STAGES, int WAVES_M, int WAVES_N, int OUT_DT, int EPI, bool kSplit>
+template <int BM, int BN, int STAGES, int WAVES_M, int WAVES_N, int OUT_DT, int EPI, bool kSplit, int KB = kDBK>
 static void launch_dma_t(const void* A, const void* B, void* C, float* partial, int M, int N, int K, int splits,
                          int k_per_split, hipStream_t s) {
   const int tilesM = (int)cdiv(M, BM), tilesN = (int)cdiv(N, BN);
-  hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, STAGES, WAVES_M, WAVES_N, OUT_DT, EPI, kSplit>), dim3(tilesM * tilesN, splits),
+  hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, STAGES, WAVES_M, WAVES_N, OUT_DT, EPI, kSplit, KB>), dim3(tilesM * tilesN, splits),
                      dim3(64 * WAVES_M * WAVES_N),
                      0, s, static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), C, partial, M, N, K,
                      tilesM, tilesN, k_per_split);
@@ -544,8 +556,17 @@ static void launch_dma(DmaTile t, const void* A, const void* B, void* C, float* 
     launch_dma_t<BIV_GEMM_L_TILE, OUT_DT, EPI, kSplit>(A, B, C, partial, M, N, K, splits, k_per_split, s);
   else if (t == kTileS)
     launch_dma_t<BIV_GEMM_S_TILE, OUT_DT, EPI, kSplit>(A, B, C, partial, M, N, K, splits, k_per_split, s);
-  else if (t == kTileQ)
-    launch_dma_t<BIV_GEMM_Q_TILE, OUT_DT, EPI, kSplit>(A, B, C, partial, M, N, K, splits, k_per_split, s);
+  else if (t == kTileQ) {
+    // 256-byte row copies (128-wide k stages) where K allows; split-K
+    // ranges are multiples of 64
+    if constexpr (!kSplit) {
+      if (K % 128 == 0) {
+        launch_dma_t<BIV_GEMM_Q_TILE, OUT_DT, EPI, kSplit, 128>(A, B, C, partial, M, N, K, splits, k_per_split, s);
+        return;
+      }
+    }
+    launch_dma_t<BIV_GEMM_Q64_TILE, OUT_DT, EPI, kSplit>(A, B, C, partial, M, N, K, splits, k_per_split, s);
+  }
   else
     launch_dma_t<BIV_GEMM_T_TILE, OUT_DT, EPI, kSplit>(A, B, C, partial, M, N, K, splits, k_per_split, s);
 }

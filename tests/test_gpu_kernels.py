@@ -518,6 +518,33 @@ def test_gemm_bf16_tile_classes_invariance(biv, N):
         assert np.array_equal(bits(cM), full_bits[:M]), f"rows changed at M={M}, N={N}"
 
 
+@pytest.mark.parametrize("K", [4096, 4160])
+def test_gemm_bf16_tiles_and_k_widths_change_no_bits(biv, K):
+    """One weight of 6144 rows (the 128 x 96 tile class: 128-wide k stages
+    when K % 128 == 0, else 64-wide) against its column slices of 4096 and
+    2048 rows (the 128 x 64 tile, 64-wide k stages): every output element is
+    reduced in the same order whatever tile and k width hold it, so the
+    columns agree bit for bit (fp32 and bf16 outputs)."""
+    M, N = 333, 6144
+    a_np = wl.normal_bf16(140, (M, K))
+    w_np = wl.normal_bf16(141, (N, K), std=0.02)
+    a, w = dev_bf16(a_np), dev_bf16(w_np)
+    announce("gemm tiles and k widths", K)
+    for dt in (torch.float32, torch.bfloat16):
+        full = torch.empty((M, N), dtype=dt, device=DEV)
+        biv.gemm_bi(a, w, full)
+        lo = torch.empty((M, 4096), dtype=dt, device=DEV)
+        hi = torch.empty((M, N - 4096), dtype=dt, device=DEV)
+        biv.gemm_bi(a, w[:4096].contiguous(), lo)
+        biv.gemm_bi(a, w[4096:].contiguous(), hi)
+        sync()
+        fb = bits(full)
+        assert np.array_equal(bits(lo), fb[:, :4096]), f"K={K} {dt}: columns 0..4095"
+        assert np.array_equal(bits(hi), fb[:, 4096:]), f"K={K} {dt}: columns 4096.."
+    ref = oracle.linear(oracle.as_f64(a_np, "bf16"), oracle.as_f64(w_np, "bf16"))
+    check_bf16(f64(full), ref, f"gemm tiles K={K}")
+
+
 @pytest.mark.parametrize("M,N,K", [(77, 200, 264), (1, 130, 8), (129, 257, 1000), (300, 128, 4096)])
 def test_gemm_bf16_ragged_shapes(biv, M, N, K):
     a_np = wl.normal_bf16(20 + M, (M, K))
