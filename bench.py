@@ -56,6 +56,10 @@ def parse():
     p.add_argument("--attn-only", action="store_true",
                    help="only the pass's attention call (same contexts, pages and shapes) and a 512 MiB copy, "
                         "--iters times each: the program the HBM traffic counters are collected on")
+    p.add_argument("--gemm-only", action="store_true",
+                   help="only the pass's matmuls at W = 512 rows (QKV, O + residual, gate/up + SwiGLU, down + "
+                        "residual, lm_head + Gumbel epilogue), two weight copies each, --iters times each: the "
+                        "program the MFMA counters are collected on")
     return p.parse_args()
 
 
@@ -122,6 +126,60 @@ def attn_only(args):
     algo = float(np.sum(ctx.astype(np.int64) + K_CAND)) * sh.kv_heads * sh.head_dim * 2 * 2
     print(json.dumps({"attn_only": True, "launches": args.iters, "algorithmic_bytes_per_launch": algo,
                       "copy_bytes": 512 << 20, "attention_hip_sha256": _attn_source_hash()}), flush=True)
+
+
+def gemm_only(args):
+    """The pass's five matmuls at W = 512 rows with the pass's weight shapes
+    (N(0, 0.02) bf16, two copies each so that consecutive calls read other
+    weights, as consecutive layers do), each called --iters times in turn.
+    Prints the per-call algorithmic FLOP and the mean HIP-event time of each
+    matmul on the stream it runs on."""
+    import torch
+
+    import invariant_verify_verifier_amd as biv
+    import workloads as wl
+
+    torch.cuda.set_device(0)
+    sh = wl.LLAMA3_8B
+    W, H, F, V = N_REQ * K_CAND, sh.hidden, sh.ffn, sh.vocab
+    bf = torch.bfloat16
+    x = wl._torch_normal((W, H), 50, 0, 1.0, "cuda", bf)
+    xf = wl._torch_normal((W, F), 50, 1, 1.0, "cuda", bf)
+    res = torch.zeros((W, H), dtype=torch.float32, device="cuda")
+    mk = lambda shape, s: [wl._torch_normal(shape, 51, s + c, 0.02, "cuda", bf) for c in range(2)]
+    w = dict(qkv=mk((sh.qkv_out, H), 0), o=mk((H, sh.heads * sh.head_dim), 2), gu=[biv.pack_gate_up(t) for t in mk((2 * F, H), 4)],
+             down=mk((H, F), 6), head=mk((V, H), 8))
+    qkv = torch.empty((W, sh.qkv_out), dtype=bf, device="cuda")
+    act = torch.empty((W, F), dtype=bf, device="cuda")
+    noise = torch.zeros((W, V), dtype=torch.float32, device="cuda")
+    cand = torch.zeros((N_REQ, K_CAND), dtype=torch.int32, device="cuda")
+    tgt = torch.empty_like(cand)
+    acc = torch.empty(N_REQ, dtype=torch.int32, device="cuda")
+    nxt = torch.empty_like(acc)
+    gws = torch.empty(biv.gumbel_workspace_bytes(W, V), dtype=torch.uint8, device="cuda")
+    calls = {
+        "qkv": (lambda i: biv.gemm_bi(x, w["qkv"][i % 2], qkv), 2.0 * W * H * sh.qkv_out),
+        "o": (lambda i: biv.gemm_bi(x, w["o"][i % 2], res, accumulate=True), 2.0 * W * H * H),
+        "gate_up_swiglu": (lambda i: biv.gemm_bi(x, w["gu"][i % 2], act, swiglu=True), 2.0 * W * H * 2 * F),
+        "down": (lambda i: biv.gemm_bi(xf, w["down"][i % 2], res, accumulate=True), 2.0 * W * F * H),
+        "lm_head_gumbel": (lambda i: biv.lm_head_gumbel_verify(x, w["head"][i % 2], noise, cand, tgt, acc, nxt, gws),
+                           2.0 * W * H * V),
+    }
+    out = {}
+    for name, (fn, flop) in calls.items():
+        for i in range(3):
+            fn(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(args.iters):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.iters
+        out[name] = {"flop": flop, "us": round(ms * 1000, 2), "tflops": round(flop / ms / 1e9, 1),
+                     "frac_of_2500": round(flop / ms / 1e9 / 2500.0, 3)}
+        print(f"[gemm-only] {name}: {out[name]}", file=sys.stderr, flush=True)
+    print(json.dumps({"gemm_only": True, "M": W, "calls_per_matmul": args.iters + 3, "matmuls": out}), flush=True)
 
 
 class EventTimer:
@@ -652,6 +710,9 @@ def main():
         return
     if args.attn_only and args.gpus == 1:
         attn_only(args)
+        return
+    if args.gemm_only and args.gpus == 1:
+        gemm_only(args)
         return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
