@@ -229,3 +229,18 @@ def test_round_bf16_matches_bit_level_rne_on_fp32_values():
     np.testing.assert_array_equal(oracle.round_bf16(x.astype(np.float64)), ref)
     assert oracle.round_bf16(np.array([1 + 2 ** -8]))[0] == 1.0       # tie to even (down)
     assert oracle.round_bf16(np.array([1 + 3 * 2 ** -8]))[0] == 1 + 2 ** -6  # tie to even (up)
+
+
+def test_silu_closed_forms():
+    """silu(z) = z * sigmoid(z), pinned by values fixed by the mathematics:
+    silu(0) = 0; sigmoid(ln 3) = 3/4 and sigmoid(-ln 3) = 1/4, so
+    silu(+-ln 3) = +-(3/4, 1/4) ln 3; silu(z) - silu(-z) = z for every z;
+    silu(z) -> z for large z and -> 0 for very negative z.  A dropped sign,
+    a missing factor z or sigmoid(-z) in place of sigmoid(z) fails one."""
+    ln3 = math.log(3.0)
+    got = oracle.silu(np.array([0.0, ln3, -ln3, 40.0, -40.0]))
+    assert got[0] == 0.0
+    assert abs(got[1] - 0.75 * ln3) < 1e-15 and abs(got[2] + 0.25 * ln3) < 1e-15
+    assert abs(got[3] - 40.0) < 1e-12 and abs(got[4]) < 1e-15
+    z = np.linspace(-9.0, 9.0, 181)
+    np.testing.assert_allclose(oracle.silu(z) - oracle.silu(-z), z, rtol=0, atol=1e-13)
