@@ -30,6 +30,7 @@ from .ops import (  # noqa: F401
     gumbel_sample,
     gumbel_topk,
     gumbel_verify,
+    kv_copy_pages,
     kv_overwrite,
     linear,
     perturbed_scores,
@@ -40,4 +41,6 @@ from .ops import (  # noqa: F401
     sequential_decode,
     silu,
     dvr_decode,
+    tree_select,
+    tree_verify,
 )

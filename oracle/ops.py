@@ -313,3 +313,68 @@ def dvr_decode(w, t0, ctx, k_caches, v_caches, block_table, n_tokens, K, drafter
         for r in range(R):
             hist[r].extend(committed[r])
     return np.asarray([h[:n_tokens] for h in hist], dtype=np.int32)
+
+
+# ---------------------------------------------------------------------------
+# Tree verification by branches (Gumbel post: top-k drafts from the shared
+# noise; with the noise fixed the output does not depend on the drafter).  A
+# draft tree is given as B root-to-leaf chains per request; every chain is
+# checked as an ordinary verifier row block on its own copy of the pages that
+# hold positions L_r .. L_r+K-1.
+# ---------------------------------------------------------------------------
+
+
+def kv_copy_pages(k_cache, v_cache, src, dst):
+    """Page dst[i] <- page src[i] of one layer's caches (every head, all 16
+    slots, K and V), in place."""
+    for s_, d_ in zip(src, dst):
+        k_cache[d_] = k_cache[s_]
+        v_cache[d_] = v_cache[s_]
+
+
+def tree_select(accept, nxt):
+    """accept, nxt [R, B]: per request the chain with the longest accepted
+    prefix, the lowest chain index among equals.  Returns (best, accept, next) [R]."""
+    accept = np.asarray(accept)
+    nxt = np.asarray(nxt)
+    R, B = accept.shape
+    best = np.zeros(R, dtype=np.int32)
+    for r in range(R):
+        top = max(int(a) for a in accept[r])
+        best[r] = min(b for b in range(B) if int(accept[r, b]) == top)
+    rr = np.arange(R)
+    return best, accept[rr, best].astype(np.int32), nxt[rr, best].astype(np.int32)
+
+
+def tree_verify(w, t0, ctx, k_caches, v_caches, block_table, chains, private_pages, noise, block=16):
+    """One tree verification.  chains [R, B, K]; private_pages [R, B-1, P]:
+    chain b >= 1 of request r uses them in place of the request's pages from
+    page ctx[r] // block on, the first receiving a copy of the request's page
+    ctx[r] // block; noise [R, K, V] (one row per sampled position, shared by
+    the chains).  Caches are modified in place (page copies, then each
+    chain's K/V).  Returns (best, accept, next) [R] and the chains' targets
+    [R, B, K]."""
+    chains = np.asarray(chains)
+    R, B, K = chains.shape
+    bt = np.asarray(block_table)
+    rows_bt = np.repeat(bt, B, axis=0).copy()
+    src, dst = [], []
+    for r in range(R):
+        p0 = int(ctx[r]) // block
+        n_pages = (int(ctx[r]) % block + K + block - 1) // block
+        for b in range(1, B):
+            pages = np.asarray(private_pages[r][b - 1])[:n_pages]
+            rows_bt[r * B + b, p0:p0 + n_pages] = pages
+            src.append(int(bt[r, p0]))
+            dst.append(int(pages[0]))
+    for li in range(len(k_caches)):
+        kv_copy_pages(k_caches[li], v_caches[li], src, dst)
+    t0s = np.repeat(np.asarray(t0), B)
+    flat = chains.reshape(R * B, K)
+    inp = np.concatenate([t0s[:, None], flat[:, :K - 1]], axis=1)
+    logits = decoder_forward(w, inp, np.repeat(np.asarray(ctx), B), k_caches, v_caches, rows_bt, block)
+    V = logits.shape[-1]
+    nz = np.repeat(np.asarray(noise, dtype=np.float32)[:, None], B, axis=1).reshape(R * B, K, V)
+    tgt, acc, nxt = gumbel_verify(logits.astype(np.float32).reshape(R * B, K, V), nz, flat)
+    best, a, n = tree_select(acc.reshape(R, B), nxt.reshape(R, B))
+    return best, a, n, tgt.reshape(R, B, K)

@@ -193,3 +193,91 @@ def test_dvr_is_lossless_and_drafter_invariant(K):
         out = oracle.dvr_decode(w, t0, ctx, [k.copy() for k in kcs], [v.copy() for v in vcs],
                                 lay.block_table, n, K, dr, noise)
         np.testing.assert_array_equal(out, seq[:, :n], err_msg=name)
+
+
+def _tree_world(sh, ctx, K, B, seed):
+    """Requests with random-KV contexts, their block tables (covering
+    L_r .. L_r+K-1) and (B-1) x 2 spare pages per request for the chains."""
+    lay = wl.paged_layout(ctx, K, seed=seed)
+    R = len(ctx)
+    n_priv = 2 * max(B - 1, 1)
+    nb = lay.num_blocks + R * n_priv
+    kcs, vcs = _caches(sh, nb, seed + 1)
+    priv = (lay.num_blocks + np.arange(R * n_priv)).reshape(R, n_priv)[:, :2 * (B - 1)].reshape(R, B - 1, 2)
+    return lay, kcs, vcs, priv
+
+
+def _seq_tokens(w, t0, ctx, kcs, vcs, bt, K, noise):
+    return oracle.sequential_decode(w, t0, ctx, [k.copy() for k in kcs], [v.copy() for v in vcs], bt, K, noise)
+
+
+def test_tree_of_every_chain_accepts_the_decode():
+    """Tree verification over ALL V^K chains of a micro vocabulary: exactly one
+    chain is the target's own continuation, so every request accepts all K
+    tokens, and the selected chain equals one-token-at-a-time decoding (spec-dec
+    guide: the target accepts only what it would write itself).  A wrong page
+    copy, a chain mixed up with another or a wrong selection fails this."""
+    sh = MICRO
+    K = 2
+    w = _weights64(sh, 21, std=0.6)
+    ctx = [13, 30]  # page offsets 13 and 14: positions L .. L+K-1 cross into the next page for r = 1 only
+    chains_one = np.array([[a, b] for a in range(sh.vocab) for b in range(sh.vocab)], dtype=np.int32)
+    B = len(chains_one)
+    lay, kcs, vcs, priv = _tree_world(sh, ctx, K, B, 22)
+    noise_fn = _noise_fn(23, sh.vocab)
+    t0 = np.array([4, 7])
+    noise = np.stack([np.stack([noise_fn(r, ctx[r] + j + 1) for j in range(K)]) for r in range(2)])
+    seq = _seq_tokens(w, t0, ctx, kcs, vcs, lay.block_table, K, noise_fn)
+    chains = np.stack([chains_one, chains_one])
+    best, acc, nxt, tgt = oracle.tree_verify(w, t0, ctx, kcs, vcs, lay.block_table, chains, priv, noise)
+    np.testing.assert_array_equal(acc, [K, K])
+    np.testing.assert_array_equal(nxt, [-1, -1])
+    for r in range(2):
+        np.testing.assert_array_equal(chains[r, best[r]], seq[r, :K])
+        # every chain's first target is the decode's first token (shared noise row)
+        assert (tgt[r, :, 0] == seq[r, 0]).all()
+
+
+def test_tree_commits_the_decode_prefix_of_its_best_chain():
+    """Random chains plus chains that follow the decode for d tokens and then
+    differ: the accepted length is the longest such d, the selected chain the
+    first chain reaching it, and accepted tokens + correction are the decode's
+    first d + 1 tokens (Gumbel post: the output does not depend on the
+    drafter)."""
+    sh = SMALL
+    K, B = 4, 5
+    w = _weights64(sh, 24, std=0.5)
+    ctx = [29, 16, 45]
+    lay, kcs, vcs, priv = _tree_world(sh, ctx, K, B, 25)
+    noise_fn = _noise_fn(26, sh.vocab)
+    t0 = np.array([3, 9, 17])
+    R = len(ctx)
+    noise = np.stack([np.stack([noise_fn(r, ctx[r] + j + 1) for j in range(K)]) for r in range(R)])
+    seq = _seq_tokens(w, t0, ctx, kcs, vcs, lay.block_table, K, noise_fn)
+    g = wl.rng(27)
+    chains = g.integers(0, sh.vocab, size=(R, B, K)).astype(np.int32)
+    plan = [(1, 2, 3), (0, 0, 0), (3, 1, 3)]  # per request: d of chains 1, 2 and of chain 4 (a duplicate d)
+    for r, (d1, d2, d4) in enumerate(plan):
+        for b, d in ((1, d1), (2, d2), (4, d4)):
+            chains[r, b, :d] = seq[r, :d]
+            if d < K:
+                chains[r, b, d] = (seq[r, d] + 1) % sh.vocab
+        for b in (0, 3):  # random chains may not follow the decode at all
+            if chains[r, b, 0] == seq[r, 0]:
+                chains[r, b, 0] = (seq[r, 0] + 2) % sh.vocab
+    best, acc, nxt, _ = oracle.tree_verify(w, t0, ctx, kcs, vcs, lay.block_table, chains, priv, noise)
+    np.testing.assert_array_equal(acc, [3, 0, 3])
+    np.testing.assert_array_equal(best, [4, 0, 1])
+    for r in range(R):
+        a = int(acc[r])
+        committed = list(chains[r, best[r], :a]) + ([int(nxt[r])] if a < K else [])
+        np.testing.assert_array_equal(committed, seq[r, :len(committed)])
+
+
+def test_tree_select_ties_go_to_the_lowest_chain():
+    acc = np.array([[2, 4, 4, 1], [0, 0, 0, 0], [3, 1, 3, 3]])
+    nxt = np.arange(12).reshape(3, 4)
+    best, a, n = oracle.tree_select(acc, nxt)
+    np.testing.assert_array_equal(best, [1, 0, 0])
+    np.testing.assert_array_equal(a, [4, 0, 3])
+    np.testing.assert_array_equal(n, [1, 4, 8])
