@@ -246,6 +246,38 @@ biv_status kv_overwrite(const void* k_new, const void* v_new, int64_t src_stride
                         biv_dtype dt, biv_stream stream);
 
 /* --------------------------------------------------------------------------
+ * Tree verification by branches.  A draft tree (for example the top-k tokens
+ * a drafter proposes from the shared Gumbel noise at each position, [GUMBEL]:
+ * top-k sampling comes with the Gumbel-max trick) is verified as B root-to-
+ * leaf chains per request, each chain an ordinary row block of the verifier
+ * step.  With the noise keyed by (request, absolute position), chains that
+ * share a prefix get the same targets on it, and every chain's bits are those
+ * of one-token-at-a-time decoding (batch invariance); the output therefore
+ * does not depend on the tree ([GUMBEL]: at a fixed seed the output does not
+ * depend on the drafter).  Each chain writes its K/V into private pages for
+ * positions L_r .. L_r+K-1; the selected chain's pages then take the place
+ * of the request's.
+ *
+ * kv_copy_pages: whole-page bit copies inside one layer's cache, page
+ *   dst_page[i] <- page src_page[i] (all Hkv heads, 16 tokens, K and V), so
+ *   that each chain's private page starts with the request's context tokens
+ *   of the page holding position L_r.  src_page, dst_page [n] int32 (device);
+ *   pairs with a page outside [0, num_blocks) or src == dst are skipped.  The
+ *   dst pages must be distinct and none may appear in src_page (copies run
+ *   in parallel).  Caches [num_blocks, Hkv, 16, D], 16-byte aligned.
+ *
+ * tree_select: for R requests of B chains each (accept_len, next_token
+ *   [R*B] int32, chain-major within a request, as gumbel_verify writes them
+ *   for R*B chains), best[r] = the chain with the longest accepted prefix,
+ *   the lowest chain index among equals; accept_out[r] and next_out[r] are
+ *   that chain's values.  All device pointers, [R] int32 outputs.
+ * ------------------------------------------------------------------------ */
+biv_status kv_copy_pages(const int32_t* src_page, const int32_t* dst_page, int n, void* k_cache, void* v_cache,
+                         int num_blocks, int Hkv, int D, biv_dtype dt, biv_stream stream);
+biv_status tree_select(const int32_t* accept_len, const int32_t* next_token, int R, int B, int32_t* best,
+                       int32_t* accept_out, int32_t* next_out, biv_stream stream);
+
+/* --------------------------------------------------------------------------
  * Elementwise helpers of the decoder forward (no reductions; row-local).
  * ------------------------------------------------------------------------ */
 

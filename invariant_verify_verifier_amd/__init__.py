@@ -21,6 +21,7 @@ from ._lib import (  # noqa: F401
     gumbel_topk,
     gumbel_verify,
     gumbel_workspace_bytes,
+    kv_copy_pages,
     kv_overwrite,
     lm_head_gumbel_verify,
     pack_gate_up,
@@ -31,4 +32,5 @@ from ._lib import (  # noqa: F401
     splitk_auto_splits,
     splitk_workspace_bytes,
     swiglu,
+    tree_select,
 )

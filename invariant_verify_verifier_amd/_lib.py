@@ -46,6 +46,8 @@ _SIGS = {
     "biv_gumbel_workspace_bytes": ([_i32, _i32], _sz),
     "lm_head_gumbel_verify": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
     "kv_overwrite": ([_vp, _vp, _i64, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp], _i32),
+    "kv_copy_pages": ([_vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp], _i32),
+    "tree_select": ([_vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp], _i32),
     "embed_rows": ([_vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp], _i32),
     "biv_rope_table": ([_vp, _i32, _i32, _f64], _i32),
     "rope_apply": ([_vp, _i64, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp], _i32),
@@ -212,6 +214,34 @@ def attn_decode_adaptive(q, k_cache, v_cache, block_table, ctx, out, q_len, scal
         _p(q), q_stride, _p(k_cache), _p(v_cache), _p(block_table), _p(ctx), _p(out), R, q_len, Hq, Hkv, D, max_blocks,
         num_blocks, scale, split_tokens, _p(workspace), wbytes, _stream()))
     return out
+
+
+def kv_copy_pages(src_page, dst_page, k_cache, v_cache):
+    """Whole-page copies inside one layer's cache: page dst_page[i] <- src_page[i]
+    (int32 [n] device tensors); caches [num_blocks, Hkv, 16, D]."""
+    _contig(src_page, dst_page, k_cache, v_cache)
+    _want(src_page, torch.int32, "src_page")
+    _want(dst_page, torch.int32, "dst_page")
+    assert src_page.numel() == dst_page.numel()
+    _same_dtype(k_cache, v_cache)
+    nb, Hkv, blk, D = k_cache.shape
+    assert blk == 16 and tuple(v_cache.shape) == tuple(k_cache.shape)
+    _check("kv_copy_pages", _lib.kv_copy_pages(_p(src_page), _p(dst_page), src_page.numel(), _p(k_cache), _p(v_cache),
+                                               nb, Hkv, D, _dt(k_cache), _stream()))
+
+
+def tree_select(accept_len, next_token, best, accept_out, next_out):
+    """accept_len/next_token [R, B] int32 (B chains per request); best, accept_out,
+    next_out [R] int32: the chain with the longest accepted prefix (lowest index
+    among equals) and its values."""
+    _contig(accept_len, next_token, best, accept_out, next_out)
+    for t, n in ((accept_len, "accept_len"), (next_token, "next_token"), (best, "best"),
+                 (accept_out, "accept_out"), (next_out, "next_out")):
+        _want(t, torch.int32, n)
+    R, B = accept_len.shape
+    assert tuple(next_token.shape) == (R, B) and best.numel() == R and accept_out.numel() == R and next_out.numel() == R
+    _check("tree_select", _lib.tree_select(_p(accept_len), _p(next_token), R, B, _p(best), _p(accept_out),
+                                           _p(next_out), _stream()))
 
 
 def gumbel_verify(logits, noise, cand, target, accept_len, next_token):

@@ -159,6 +159,22 @@ __global__ void swiglu_kernel(const void* __restrict__ gu, void* __restrict__ ou
   }
 }
 
+// Whole-page copies inside one layer's cache, one thread per 16 bytes of a
+// page of K and the same 16 bytes of V.  Pairs with a page outside
+// [0, num_blocks) or with src == dst are skipped.
+__global__ void kv_copy_pages_kernel(const int32_t* __restrict__ src, const int32_t* __restrict__ dst,
+                                     uint4* __restrict__ k_cache, uint4* __restrict__ v_cache, int n, int64_t page16,
+                                     int num_blocks) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)n * page16) return;
+  const int i = (int)(gid / page16);
+  const int64_t piece = gid - (int64_t)i * page16;
+  const int sp = src[i], dp = dst[i];
+  if (sp < 0 || sp >= num_blocks || dp < 0 || dp >= num_blocks || sp == dp) return;
+  k_cache[(int64_t)dp * page16 + piece] = k_cache[(int64_t)sp * page16 + piece];
+  v_cache[(int64_t)dp * page16 + piece] = v_cache[(int64_t)sp * page16 + piece];
+}
+
 }  // namespace biv
 
 extern "C" biv_status kv_overwrite(const void* k_new, const void* v_new, int64_t src_stride, const int64_t* slot,
@@ -267,4 +283,21 @@ extern "C" biv_status swiglu(const void* gu, void* out, int64_t M, int64_t N, in
   hipLaunchKernelGGL(swiglu_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), gu, out, M, N,
                      block, (int)dt);
   return launched("swiglu");
+}
+
+extern "C" biv_status kv_copy_pages(const int32_t* src_page, const int32_t* dst_page, int n, void* k_cache,
+                                    void* v_cache, int num_blocks, int Hkv, int D, biv_dtype dt, biv_stream stream) {
+  using namespace biv;
+  BIV_REQUIRE(valid_dt(dt), "kv_copy_pages: bad dtype");
+  BIV_REQUIRE(n >= 0 && num_blocks >= 1 && Hkv >= 1 && D >= 1, "kv_copy_pages: bad sizes");
+  if (n == 0) return BIV_OK;
+  BIV_REQUIRE(src_page && dst_page && k_cache && v_cache, "kv_copy_pages: NULL pointer");
+  BIV_REQUIRE(aligned16(k_cache) && aligned16(v_cache), "kv_copy_pages: caches must be 16-byte aligned");
+  const int64_t page16 = (int64_t)Hkv * 16 * D * (int64_t)dt_size(dt) / 16;  // a page is 16 tokens: whole 16-byte pieces
+  const int64_t total = (int64_t)n * page16;
+  BIV_REQUIRE(cdiv(total, 256) <= 0x7fffffff, "kv_copy_pages: too many pages");
+  hipLaunchKernelGGL(kv_copy_pages_kernel, dim3((unsigned)cdiv(total, 256)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), src_page, dst_page, static_cast<uint4*>(k_cache),
+                     static_cast<uint4*>(v_cache), n, page16, num_blocks);
+  return launched("kv_copy_pages");
 }

@@ -264,6 +264,28 @@ biv_status launch_gumbel_finish(const uint2* part, int groups, const int32_t* ca
 
 }  // namespace biv
 
+namespace biv {
+// One thread per request: the branch with the longest accepted prefix, the
+// lowest branch index among equals.
+__global__ void tree_select_kernel(const int32_t* __restrict__ accept_len, const int32_t* __restrict__ next_token,
+                                   int R, int B, int32_t* __restrict__ best, int32_t* __restrict__ accept_out,
+                                   int32_t* __restrict__ next_out) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= R) return;
+  const int32_t* a = accept_len + (int64_t)r * B;
+  int bb = 0, ba = a[0];
+  for (int b = 1; b < B; ++b) {
+    if (a[b] > ba) {
+      ba = a[b];
+      bb = b;
+    }
+  }
+  best[r] = bb;
+  accept_out[r] = ba;
+  next_out[r] = next_token[(int64_t)r * B + bb];
+}
+}  // namespace biv
+
 extern "C" biv_status gumbel_verify(const float* logits, const float* noise, const int32_t* cand, int R,
                                     int K, int V, int32_t* target, int32_t* accept_len,
                                     int32_t* next_token, biv_stream stream) {
@@ -301,4 +323,16 @@ extern "C" biv_status gumbel_topk(const float* logits, const float* noise, int r
     hipLaunchKernelGGL(gumbel_topk_kernel<false>, dim3((unsigned)rows), dim3(kVerifyThreads), 0, s, logits, noise, V,
                        k, idx, score);
   return launched("gumbel_topk");
+}
+
+extern "C" biv_status tree_select(const int32_t* accept_len, const int32_t* next_token, int R, int B, int32_t* best,
+                                  int32_t* accept_out, int32_t* next_out, biv_stream stream) {
+  using namespace biv;
+  BIV_REQUIRE(R >= 0 && B >= 1, "tree_select: need R >= 0 and B >= 1 (R=%d B=%d)", R, B);
+  BIV_REQUIRE((int64_t)R * B <= 0x7fffffff, "tree_select: too many branches");
+  if (R == 0) return BIV_OK;
+  BIV_REQUIRE(accept_len && next_token && best && accept_out && next_out, "tree_select: NULL pointer");
+  hipLaunchKernelGGL(tree_select_kernel, dim3((unsigned)cdiv(R, 64)), dim3(64), 0, static_cast<hipStream_t>(stream),
+                     accept_len, next_token, R, B, best, accept_out, next_out);
+  return launched("tree_select");
 }

@@ -263,6 +263,76 @@ def make_batch(t0, cand, ctx, block_table, noise, device="cuda") -> VerifyBatch:
         next_token=torch.empty(R, dtype=torch.int32, device=device))
 
 
+@dataclass
+class TreeBatch:
+    """A verifier step over B chains per request (tree verification by
+    branches): ``chains`` is the VerifyBatch of the R*B chains, chain b of
+    request r at row block r*B + b; the page copies give every chain after the
+    first a private copy of the page holding position L_r (and private pages
+    for the rest of L_r .. L_r+K-1)."""
+
+    R: int
+    B: int
+    chains: VerifyBatch
+    copy_src: torch.Tensor  # [n] int32 pages copied into ...
+    copy_dst: torch.Tensor  # [n] int32 ... the chains' private pages
+    best: torch.Tensor  # [R] int32 outputs of tree_select
+    accept_len: torch.Tensor
+    next_token: torch.Tensor
+
+
+def make_tree_batch(t0, chains, ctx, block_table, private_pages, noise, device="cuda") -> TreeBatch:
+    """Host bookkeeping for tree verification by branches.
+
+    chains [R, B, K] int32: the candidate tokens of each root-to-leaf chain of
+    request r's draft tree (chains may share prefixes).  block_table [R, mb]:
+    the requests' tables, covering positions up to L_r + K - 1 (chain 0 uses
+    them as they are).  private_pages [R, B-1, P] int32: for chains 1..B-1,
+    the P = ceil((L_r % 16 + K) / 16) pages that replace the request's pages
+    from page L_r // 16 on; the first of them receives a copy of the request's
+    page L_r // 16 (its context tokens).  noise [R, K, V]: the noise row of
+    the position each output samples, shared by all chains of a request (the
+    key is the request and the absolute position)."""
+    chains = np.asarray(chains, dtype=np.int32)
+    R, B, K = chains.shape
+    ctx = np.asarray(ctx, dtype=np.int32)
+    bt = np.asarray(block_table, dtype=np.int32)
+    priv = np.asarray(private_pages, dtype=np.int32).reshape(R, B - 1, -1) if B > 1 else None
+    rows_bt = np.repeat(bt, B, axis=0).copy()  # [R*B, mb]
+    src, dst = [], []
+    for r in range(R):
+        p0 = int(ctx[r]) // 16
+        n_pages = (int(ctx[r]) % 16 + K + 15) // 16
+        for b in range(1, B):
+            pages = priv[r, b - 1, :n_pages]
+            rows_bt[r * B + b, p0:p0 + n_pages] = pages
+            src.append(int(bt[r, p0]))
+            dst.append(int(pages[0]))
+    t0s = np.repeat(np.asarray(t0, dtype=np.int32), B)
+    nz = noise if isinstance(noise, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(noise, dtype=np.float32))
+    nz = nz.reshape(R, 1, K, -1).expand(R, B, K, nz.shape[-1]).reshape(R * B * K, -1).contiguous()
+    cb = make_batch(t0s, chains.reshape(R * B, K), np.repeat(ctx, B), rows_bt, nz, device=device)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(np.asarray(a, dtype=np.int32))).to(device)
+    return TreeBatch(R=R, B=B, chains=cb, copy_src=dev(src), copy_dst=dev(dst),
+                     best=torch.empty(R, dtype=torch.int32, device=device),
+                     accept_len=torch.empty(R, dtype=torch.int32, device=device),
+                     next_token=torch.empty(R, dtype=torch.int32, device=device))
+
+
+def verify_tree(model, tb: TreeBatch, caches, **kw):
+    """One verifier step over every chain of every request's draft tree: copy
+    the context page into the chains' private pages (every layer), run the
+    ordinary verifier step over the R*B chains, then pick each request's chain
+    with the longest accepted prefix.  Returns (best [R], accept_len [R],
+    next_token [R], per-chain targets [R*B, K])."""
+    if tb.copy_src.numel():
+        for k_cache, v_cache in caches:
+            L.kv_copy_pages(tb.copy_src, tb.copy_dst, k_cache, v_cache)
+    _, target, acc, nxt = model.verify(tb.chains, caches, **kw)
+    L.tree_select(acc.view(tb.R, tb.B), nxt.view(tb.R, tb.B), tb.best, tb.accept_len, tb.next_token)
+    return tb.best, tb.accept_len, tb.next_token, target
+
+
 def self_consistent_candidates(model, t0, ctx, block_table, noise, caches, K, first=None, **kw):
     """Candidates that equal the verifier's own targets at every position.
 
