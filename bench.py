@@ -56,6 +56,10 @@ def parse():
     p.add_argument("--attn-only", action="store_true",
                    help="only the pass's attention call (same contexts, pages and shapes) and a 512 MiB copy, "
                         "--iters times each: the program the HBM traffic counters are collected on")
+    p.add_argument("--tree", action="store_true",
+                   help="instead of the pass: tree verification by branches at the pass's shape, --branches chains "
+                        "per request (each an ordinary row block; W = N*B*K rows), graph-replayed")
+    p.add_argument("--branches", default="1,2,4", help="chains per request in --tree")
     p.add_argument("--gemm-only", action="store_true",
                    help="only the pass's matmuls at W = 512 rows (QKV, O + residual, gate/up + SwiGLU, down + "
                         "residual, lm_head + Gumbel epilogue), two weight copies each, --iters times each: the "
@@ -126,6 +130,69 @@ def attn_only(args):
     algo = float(np.sum(ctx.astype(np.int64) + K_CAND)) * sh.kv_heads * sh.head_dim * 2 * 2
     print(json.dumps({"attn_only": True, "launches": args.iters, "algorithmic_bytes_per_launch": algo,
                       "copy_bytes": 512 << 20, "attention_hip_sha256": _attn_source_hash()}), flush=True)
+
+
+def tree_bench(args):
+    """Tree verification by branches at the pass's shape: N = 64 requests,
+    K = 8, contexts U[2048, 8192], B chains per request.  Chain b of request r
+    follows the target's own tokens for d[r, b] ~ U{0..K} tokens and then
+    differs, so the accepted length must be max_b d[r, b] and the selected
+    chain the first reaching it (checked before timing).  The step (page
+    copies for every layer, the verifier step over N*B chains with the fused
+    lm_head + Gumbel verification, chain selection) is captured as one HIP
+    graph and replayed --steps times."""
+    import torch
+
+    from invariant_verify_verifier_amd import verifier as V
+    import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    Bs = [int(b) for b in args.branches.split(",")]
+    extra = N_REQ * 2 * (max(Bs) - 1)
+    print(f"[tree] setup: {args.layers} layers, {N_REQ} requests x K={K_CAND}, chains {Bs}", file=sys.stderr, flush=True)
+    env = setup(torch, args.layers, extra_blocks=extra)
+    model, caches, ctx, lay, tgt = env["model"], env["caches"], env["ctx"], env["lay"], env["tgt"]
+    sh = env["sh"]
+    results = {}
+    for B in Bs:
+        g = wl.rng(wl.SEEDS["pass_tokens"] + 10 + B)
+        d = g.integers(0, K_CAND + 1, size=(N_REQ, B))
+        chains = np.stack([wl.plant_divergence(tgt, d[:, b], sh.vocab, wl.SEEDS["pass_tokens"] + 20 + b)
+                           for b in range(B)], axis=1)
+        priv = (lay.num_blocks + np.arange(N_REQ * 2 * (B - 1))).reshape(N_REQ, B - 1, 2) if B > 1 else None
+        tb = V.make_tree_batch(env["t0"], chains, ctx, lay.block_table, priv, env["noise"])
+        best, acc, nxt, _ = V.verify_tree(model, tb, caches, fused_head=True)
+        torch.cuda.synchronize()
+        want_acc = d.max(axis=1)
+        assert np.array_equal(acc.cpu().numpy(), want_acc), "accepted lengths differ from the planted ones"
+        assert np.array_equal(best.cpu().numpy(), d.argmax(axis=1)), "selected chains differ"
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            V.verify_tree(model, tb, caches, fused_head=True)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(tb.accept_len.cpu().numpy(), want_acc), "graph replay changed the decisions"
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        committed = float(np.mean(np.minimum(want_acc + 1, K_CAND)))
+        results[B] = {"rows": N_REQ * B * K_CAND, "ms_per_step": round(ms, 3),
+                      "verified_rows_per_s": round(N_REQ * B * K_CAND / ms * 1000, 1),
+                      "mean_accepted": float(np.mean(want_acc)), "mean_committed_per_request": committed,
+                      "committed_tok_per_s": round(N_REQ * committed / ms * 1000, 1)}
+        print(f"[tree] B={B}: {results[B]}", file=sys.stderr, flush=True)
+        del graph, tb
+        torch.cuda.empty_cache()
+    print(json.dumps({"tree": True, "N": N_REQ, "K": K_CAND, "layers": args.layers,
+                      "workload": "Llama-3-8B-shaped verifier step over B chains per request, contexts U[2048,8192], "
+                                  "chains planted with d ~ U{0..K} accepted tokens each",
+                      "branches": results}), flush=True)
 
 
 def gemm_only(args):
@@ -208,7 +275,7 @@ class EventTimer:
         return float(np.mean([s.elapsed_time(e) for s, e in self.pairs])) if self.pairs else float("nan")
 
 
-def setup(torch, n_layers):
+def setup(torch, n_layers, extra_blocks=0):
     import workloads as wl
     from invariant_verify_verifier_amd import verifier as V
 
@@ -216,7 +283,7 @@ def setup(torch, n_layers):
     ctx = wl.context_lengths(wl.SEEDS["pass_len"], N_REQ, CTX_LO, CTX_HI)
     lay = wl.paged_layout(ctx, K_CAND, seed=wl.SEEDS["pass_len"] + 1)
     dw = wl.device_model_weights(sh, wl.SEEDS["pass_weights"], layers=n_layers)
-    caches = wl.device_kv_cache(sh, lay.num_blocks, wl.SEEDS["pass_kv"], layers=n_layers)
+    caches = wl.device_kv_cache(sh, lay.num_blocks + extra_blocks, wl.SEEDS["pass_kv"], layers=n_layers)
     shape = V.Shape(n_layers, sh.hidden, sh.heads, sh.kv_heads, sh.head_dim, sh.ffn, sh.vocab, sh.eps,
                     sh.rope_theta)
     model = V.VerifierModel(shape, torch.bfloat16, dw["layers"], dw["embed"], dw["lm_head"], dw["final_norm"],
@@ -233,7 +300,7 @@ def setup(torch, n_layers):
     cand = wl.plant_divergence(tgt, d, sh.vocab, wl.SEEDS["pass_tokens"] + 2)
     batch = V.make_batch(t0, cand, ctx, lay.block_table, noise)
     return dict(sh=sh, ctx=ctx, lay=lay, dw=dw, caches=caches, model=model, batch=batch, d=d, t0=t0, cand=cand,
-                noise=noise)
+                noise=noise, tgt=tgt)
 
 
 def time_graph(torch, model, batch, caches, steps, warmup, **kw):
@@ -713,6 +780,9 @@ def main():
         return
     if args.gemm_only and args.gpus == 1:
         gemm_only(args)
+        return
+    if args.tree and args.gpus == 1:
+        tree_bench(args)
         return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
