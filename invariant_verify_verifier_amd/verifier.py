@@ -333,6 +333,34 @@ def verify_tree(model, tb: TreeBatch, caches, **kw):
     return tb.best, tb.accept_len, tb.next_token, target
 
 
+def adopt_chain_pages(block_table, ctx, best, private_pages, K):
+    """Host bookkeeping after tree verification: request r keeps the pages of
+    its selected chain best[r] for positions L_r .. L_r+K-1 (chain 0 uses the
+    request's own pages; chain b >= 1 its private ones, whose first page
+    already holds a copy of the request's context tokens).  Returns the new
+    block table [R, mb] and, per request, the pages no longer in use (the
+    request's replaced pages and the other chains' private pages)."""
+    bt = np.array(block_table, dtype=np.int32, copy=True)
+    ctx = np.asarray(ctx)
+    best = np.asarray(best)
+    R = bt.shape[0]
+    priv = None if private_pages is None else np.asarray(private_pages, dtype=np.int32)
+    freed = []
+    for r in range(R):
+        p0 = int(ctx[r]) // 16
+        n_pages = (int(ctx[r]) % 16 + K + 15) // 16
+        b = int(best[r])
+        mine = [] if priv is None else [int(x) for x in priv[r].reshape(priv.shape[1], -1)[:, :n_pages].ravel()]
+        if b > 0:
+            chosen = [int(x) for x in priv[r, b - 1, :n_pages]]
+            out = [int(x) for x in bt[r, p0:p0 + n_pages]] + [x for x in mine if x not in chosen]
+            bt[r, p0:p0 + n_pages] = chosen
+        else:
+            out = mine
+        freed.append(out)
+    return bt, freed
+
+
 def self_consistent_candidates(model, t0, ctx, block_table, noise, caches, K, first=None, **kw):
     """Candidates that equal the verifier's own targets at every position.
 

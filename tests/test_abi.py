@@ -151,3 +151,22 @@ def test_dvr_round_stats_and_rollback_rule():
     st.accept_len.append(acc)
     st.committed.append(np.array([len(c) for c in committed]))
     assert st.acceptance(4) == 0.5 and abs(st.tokens_per_round() - 8 / 3) < 1e-12
+
+
+def test_tree_adopt_chain_pages_host_rule():
+    """After tree verification a request keeps its selected chain's pages for
+    L .. L+K-1 and frees the rest (host bookkeeping; no GPU)."""
+    import numpy as np
+
+    from invariant_verify_verifier_amd import verifier as V
+
+    bt = np.array([[0, 1, 2, 3], [4, 5, 6, 7]], np.int32)
+    ctx = [20, 35]  # request 0: positions 20..23 on page 1; request 1: 35..38 on page 2
+    priv = np.array([[[10, 11], [12, 13]], [[14, 15], [16, 17]]], np.int32)  # [R, B-1, 2]
+    nbt, freed = V.adopt_chain_pages(bt, ctx, [2, 0], priv, K=4)
+    assert nbt.tolist() == [[0, 12, 2, 3], [4, 5, 6, 7]]
+    assert sorted(freed[0]) == [1, 10] and sorted(freed[1]) == [14, 16]
+    # a span over two pages (L % 16 + K > 16) moves both
+    nbt, freed = V.adopt_chain_pages(bt, [30, 0], [1, 1], priv, K=4)
+    assert nbt.tolist() == [[0, 10, 11, 3], [14, 5, 6, 7]]
+    assert sorted(freed[0]) == [1, 2, 12, 13] and sorted(freed[1]) == [4, 16]

@@ -9,7 +9,9 @@ path's).
 * a tree of B chains per request on the tiny fp32 decoder: decisions equal
   the oracle's tree verification, the selected chain's targets and K/V equal,
   bit for bit, the same chain verified on its own with the request's own
-  pages, and accepted tokens + correction are one-token-at-a-time decoding.
+  pages, and accepted tokens + correction are one-token-at-a-time decoding;
+  after the request adopts its selected chain's pages, the next verifier
+  round gives the same bits as after the single-chain round.
 """
 import numpy as np
 import pytest
@@ -85,7 +87,7 @@ def test_tree_verify_tiny_matches_oracle_and_single_chains(biv):
     w = wl.model_weights(TINY, wl.SEEDS["tiny_weights"], "f32")
     ow = _oracle_weights(w)
     model = V.VerifierModel.from_host(w, max_pos=1024)
-    lay = wl.paged_layout(ctx, K, seed=41)
+    lay = wl.paged_layout(ctx, 2 * K, seed=41)  # room for a second round
     priv = (lay.num_blocks + np.arange(R * (B - 1) * 2)).reshape(R, B - 1, 2).astype(np.int32)
     nb = lay.num_blocks + priv.size
     kc = [wl.normal_f32(42, (nb, TINY.kv_heads, 16, TINY.head_dim), stream=(li, 0)) for li in range(TINY.layers)]
@@ -154,3 +156,18 @@ def test_tree_verify_tiny_matches_oracle_and_single_chains(biv):
                 for t, src in ((0, kc), (1, vc)):
                     got = bits(cs[li][t][mine0, :, :int(ctx[r]) % 16])
                     assert np.array_equal(got, bits(torch.from_numpy(src[li][own0, :, :int(ctx[r]) % 16])))
+
+    # next round: the request adopts the selected chain's pages; the round
+    # after it must see the same K/V as after the single-chain round
+    new_bt, _ = V.adopt_chain_pages(lay.block_table, ctx, best, priv, K)
+    ctx2, _, t02 = V.rollback(ctx, acc, nxt, chains[np.arange(R), best])
+    cand2 = wl.tokens(46, (R, K), TINY.vocab)
+    noise2 = wl.gumbel_noise(nseed, np.repeat(np.arange(R), K).reshape(R, K), ctx2[:, None] + np.arange(K) + 1,
+                             TINY.vocab)
+    announce("tree verify: second round after adopting pages")
+    _, ta, aa, na = model.verify(V.make_batch(t02, cand2, ctx2, new_bt, noise2), cs)
+    ta, aa, na = ta.cpu().numpy(), aa.cpu().numpy(), na.cpu().numpy()
+    _, tb_, ab, nb_ = model.verify(V.make_batch(t02, cand2, ctx2, lay.block_table, noise2), cs1)
+    sync()
+    assert np.array_equal(ta, tb_.cpu().numpy()) and np.array_equal(aa, ab.cpu().numpy())
+    assert np.array_equal(na, nb_.cpu().numpy())
