@@ -140,9 +140,15 @@ biv_status gemm_bi(const void* A, const void* B, void* C, int64_t M, int64_t N, 
  * row's result depends only on its own request's data and length.
  * Positions >= ctx[r] + q_len read as empty (values zero, keys masked).
  * Two launches: the chunk/segment pass, then (only when some request spans
- * more than one segment) the fold of the segment results; large grids add
- * a one-workgroup launch before them that orders the segments.  The fp32 path
- * folds all chunk partials of a row in one ascending left fold (one launch).
+ * more than one segment, or segments are split) the fold of the partials;
+ * large grids add a one-workgroup launch before them that orders the
+ * segments.  Where the grid of segments would hold fewer than 1024 waves
+ * (decided by R, Hkv and max_blocks alone), each segment is taken by
+ * several waves over consecutive 256-token chunks: the first folds its
+ * chunks, the later ones store their chunk partials, and the second launch
+ * folds those on in the same ascending order -- the same fold, so the same
+ * bits.  The fp32 path folds all chunk partials of a row in one ascending
+ * left fold (one launch).
  *
  * Supported: dt BIV_BF16 with D == 128 and Hq/Hkv dividing 32 (bf16 MFMA
  * path; any q_len: the rows of a request are taken 32/(Hq/Hkv) positions at a
@@ -157,13 +163,14 @@ biv_status gemm_bi(const void* A, const void* B, void* C, int64_t M, int64_t N, 
  * bytes (equal to biv_attn_workspace_bytes(R, Hkv, max_blocks, ...) when
  * q_len * Hq/Hkv <= 32),
  * 16-byte aligned (bf16 path; may be NULL for the fp32 path); it holds the
- * segment results between the two launches and, for grids of at least four
- * rounds of resident waves, the work list that launches the segments in
- * longest-first order (same results); it needs no initialisation.
+ * segment (and, for split segments, chunk) partials between the two
+ * launches and, for grids of at least four rounds of resident waves, the
+ * work list that launches the segments in longest-first order (same
+ * results); it needs no initialisation.
  * Calls that share a workspace must be ordered (same stream).
  * ------------------------------------------------------------------------ */
 #define BIV_ATTN_CHUNK_TOKENS 256
-#define BIV_ATTN_SEG_TOKENS 2048
+#define BIV_ATTN_SEG_TOKENS 4096
 
 size_t biv_attn_workspace_bytes(int R, int Hkv, int max_blocks, int seg_tokens);
 /* The same for any q_len: R requests of q_len rows (0 for unsupported shapes). */

@@ -9,7 +9,8 @@
 //
 // bf16 path.  The keys of a request are cut at fixed absolute positions:
 //   sub-tile = 32 keys (one MFMA block), chunk = 256 keys (the KV split),
-//   segment  = seg_tokens keys (2048 for the invariant kernel).
+//   segment  = seg_tokens keys (4096 for the invariant kernel), taken by one
+//              wave, or split over several at small batch (see the kernel).
 // One 64-lane wave per (segment, KV head, row block), four per CU.  The rows
 // of one KV head in a row block (32/G positions x G query heads) share one
 // 32-row MFMA block, so the K/V of a page is read once for all of them (the
@@ -44,6 +45,7 @@ constexpr int kSubsPerChunk = kChunk / kSub;
 constexpr int kSlot = kSub * kHD * 2;    // 8 KiB: K or V of one sub-tile
 constexpr int kRing = 5;                 // LDS slots per wave (40 KiB: four waves fill a CU's 160 KiB)
 constexpr int kPagesPerWin = 64;         // page ids held in one register (lane i: page i of the window)
+constexpr int kPreWin = 4;               // page windows loaded at a wave's start (4096 tokens)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.0f;            // max drift (log2) before the accumulators are rescaled
 
@@ -57,12 +59,30 @@ __device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp
 // distinct bank groups.
 __device__ __forceinline__ int kv_swz(int k) { return ((k & 3) << 2) | ((k >> 2) & 3); }
 
-__device__ __forceinline__ int pick_window(int w, int w0, int w1, int wx) { return w == 0 ? w0 : (w == 1 ? w1 : wx); }
+__device__ __forceinline__ int pick_window(int w, int w0, int w1, int w2, int w3, int wx) {
+  return w == 0 ? w0 : (w == 1 ? w1 : (w == 2 ? w2 : (w == 3 ? w3 : wx)));
+}
 
 struct AttnWs {
   float* part_o;   // [slot][16 groups][64 lanes][4]: values 4q .. 4q+3 of a lane in group q
   float* part_ml;  // [slot][64 lanes][2]
+  float* chunk_o;  // chunk partials of split segments, same layout, slot (v, KV head, chunk)
+  float* chunk_ml;
 };
+
+// Partial (m, l, o[64]) of a lane -> slot `slot` of (po, pml): sixteen 1 KiB
+// streaming stores of four values each, then m and l.
+__device__ __forceinline__ void store_partial(float* po, float* pml, int64_t slot, int lane, float m, float l,
+                                              const float* o) {
+  float* so = po + slot * 4096;
+#pragma unroll
+  for (int qg = 0; qg < 16; ++qg) {
+    const f32x4 w = {o[4 * qg + 0], o[4 * qg + 1], o[4 * qg + 2], o[4 * qg + 3]};
+    __builtin_nontemporal_store(w, reinterpret_cast<f32x4*>(so + (qg * 64 + lane) * 4));
+  }
+  pml[slot * 128 + lane * 2 + 0] = m;
+  pml[slot * 128 + lane * 2 + 1] = l;
+}
 
 // Wait until at most 8n direct-to-LDS copies (n loads) are outstanding.
 __device__ __forceinline__ void wait_loads_after(int n) {
@@ -75,16 +95,21 @@ __device__ __forceinline__ void wait_loads_after(int n) {
   }
 }
 
-// (M, L, O) <- fold((M, L, O), (m, l, o)) over N outputs.
+// (M, L, O) <- fold((M, L, O), (m, l, o)) over N outputs.  The products
+// and sums are written as one explicit fused multiply-add of a rounded
+// product (o*b + round(O*a)), which the compiler cannot fuse differently
+// from one kernel to the other: the fold gives the same bits in both
+// kernels that run it (a chunk is folded in the first pass, or, in a split
+// segment, in the second).
 template <int N>
 __device__ __forceinline__ void fold_into(float& M, float& L, float* O, float m, float l, const float* o) {
   const float mn = fmaxf(M, m);
   if (mn == -INFINITY) return;  // both empty
   const float a = exp2f(M - mn);  // 0 when M == -inf, exactly 1 when M == mn
   const float b = exp2f(m - mn);
-  L = __fadd_rn(__fmul_rn(L, a), __fmul_rn(l, b));
+  L = fmaf(l, b, L * a);
 #pragma unroll
-  for (int k = 0; k < N; ++k) O[k] = __fadd_rn(__fmul_rn(O[k], a), __fmul_rn(o[k], b));
+  for (int k = 0; k < N; ++k) O[k] = fmaf(o[k], b, O[k] * a);
   M = mn;
 }
 
@@ -96,17 +121,24 @@ __device__ __forceinline__ void fold_into(float& M, float& L, float* O, float m,
 // S^T = K Q^T and O^T = V^T P^T with the 32x32x16 bf16 MFMA (its column),
 // keeps the chunk partial (m, l, o) and the segment result (M, L, O) of its
 // row in registers, and folds each finished chunk into the segment result.
+template <bool kParts>
 __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx,
     uint16_t* __restrict__ out, int q_len, int Hq, int Hkv, int max_blocks, int num_blocks, float scale_log2,
-    int seg_tokens, int nseg_max, AttnWs ws, const int32_t* __restrict__ items, int blk_pos, int n_rb) {
+    int seg_tokens, int nseg_max, AttnWs ws, const int32_t* __restrict__ items, int blk_pos, int n_rb, int parts) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kRing * kSlot];
-  // grid: (segment, KV head, row block), or with a work list a 1-D grid of
-  // (list entry, KV head), KV head fastest; an entry is v * nseg_max + seg.
-  // Row block v = r * n_rb + b holds query positions b*blk_pos .. +blk_pos-1
-  // of request r (one block, v = r, whenever q_len * G <= 32).
-  int seg, kvh, v;
+  // grid: (segment part, KV head, row block), or with a work list (parts ==
+  // 1) a 1-D grid of (list entry, KV head), KV head fastest; an entry is
+  // v * nseg_max + seg.  Row block v = r * n_rb + b holds query positions
+  // b*blk_pos .. +blk_pos-1 of request r (one block, v = r, whenever
+  // q_len * G <= 32).  A segment is taken by `parts` waves, each over
+  // seg_tokens / parts consecutive tokens: the first folds its chunks into
+  // the segment's partial (the segment result when it is the only part
+  // with keys); each later one writes its chunks' partials, which the
+  // second kernel folds on in the same ascending order -- the same fold, so
+  // the same bits, for any number of parts.
+  int seg, kvh, v, part = 0;
   if (items != nullptr) {
     kvh = (int)(blockIdx.x % (unsigned)Hkv);
     const int e = items[blockIdx.x / (unsigned)Hkv];
@@ -114,23 +146,33 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
     v = e / nseg_max;
     seg = e - v * nseg_max;
   } else {
-    seg = blockIdx.x;
+    if constexpr (kParts) {
+      seg = (int)(blockIdx.x / (unsigned)parts);
+      part = (int)blockIdx.x - seg * parts;
+    } else {
+      seg = blockIdx.x;
+    }
     kvh = blockIdx.y;
     v = blockIdx.z;
   }
+  const int part_tok = kParts ? seg_tokens / parts : seg_tokens;
+  const int tok_begin = seg * seg_tokens + part * part_tok;  // a multiple of kChunk
   const int r = v / n_rb, j0 = (v - r * n_rb) * blk_pos;  // request, first query position of the block
   const int lane = threadIdx.x, g = lane >> 5, li = lane & 31;
   const int G = Hq / Hkv, jn = min(blk_pos, q_len - j0), nrows = jn * G;
   const int32_t* bt = block_table + (int64_t)r * max_blocks;
-  const int page0 = seg * (seg_tokens >> 4);  // first page of the segment
+  const int page0 = tok_begin >> 4;  // first page of the part
 
-  // The context length, the segment's first page window and the queries are
+  // The context length, the part's first page windows and the queries are
   // loaded together: none depends on another, and the copies of the first
   // sub-tiles can only start once all three have landed.
   const int L = ctx[r];
-  int bt_w0 = -1, bt_w1 = -1;  // the segment's first two 64-page windows
-  if (page0 + lane < max_blocks) bt_w0 = bt[page0 + lane];
-  if (seg_tokens > kPagesPerWin * 16 && page0 + kPagesPerWin + lane < max_blocks) bt_w1 = bt[page0 + kPagesPerWin + lane];
+  int bt_w[kPreWin];  // the part's first kPreWin 64-page windows
+#pragma unroll
+  for (int w = 0; w < kPreWin; ++w) {
+    const int lp = page0 + kPagesPerWin * w + lane;
+    bt_w[w] = (part_tok > kPagesPerWin * 16 * w && lp < max_blocks) ? bt[lp] : -1;
+  }
   // this lane's query row (MFMA column li)
   const bool row_ok = li < nrows;
   const int jq = j0 + (row_ok ? li / G : 0);
@@ -150,8 +192,11 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
   const int n_tok = min(L + j0 + jn, max_blocks * 16);  // keys of the block's last row
   const int nseg = (n_tok + seg_tokens - 1) / seg_tokens;
   if (seg >= nseg) return;
-  const int tok_begin = seg * seg_tokens;  // a multiple of kChunk
-  const int tok_end = min(tok_begin + seg_tokens, n_tok);
+  const int seg_end = min((seg + 1) * seg_tokens, n_tok);  // keys of this segment end here
+  if (tok_begin >= seg_end) return;                        // a part with no keys
+  const int tok_end = min(tok_begin + part_tok, seg_end);
+  const bool split = kParts && seg_end - seg * seg_tokens > part_tok;  // the segment spans several parts
+  const bool first_part = !kParts || part == 0;
   const int nsub = (tok_end - tok_begin + kSub - 1) / kSub;
   const int total = 2 * nsub;  // loads: K(s) = 2s, V(s) = 2s + 1
   const int n_pages = (n_tok + 15) >> 4;
@@ -166,10 +211,11 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
     const int lp = page0 + kPagesPerWin * w + lane;
     return window_ids(w, lp < n_pages ? bt[lp] : -1);
   };
-  // windows 0 and 1 are loaded at the start; a later window (segments
-  // longer than 2048 tokens) is loaded when the copies enter it
-  const int pw0 = window_ids(0, bt_w0), pw1 = window_ids(1, bt_w1);
-  int pwx = -1, winx = 1;
+  // windows 0 .. kPreWin-1 are loaded at the start; a later window (parts
+  // longer than 4096 tokens) is loaded when the copies enter it
+  const int pw0 = window_ids(0, bt_w[0]), pw1 = window_ids(1, bt_w[1]);
+  const int pw2 = window_ids(2, bt_w[2]), pw3 = window_ids(3, bt_w[3]);
+  int pwx = -1, winx = kPreWin - 1;
   uint32_t valid_q = 0;  // bits 2(s%16), 2(s%16)+1: pages of sub-tile s present
 
   // Direct-to-LDS copy of one sub-tile (32 keys) of K or V: 8 copies of
@@ -182,7 +228,7 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
   // force them into private memory)
   auto window_for = [&](int j) {
     const int w = (j >> 1) >> 5;
-    if (!(j & 1) && w > winx) {  // K of the first sub-tile of window w >= 2
+    if (!(j & 1) && w > winx) {  // K of the first sub-tile of window w >= kPreWin
       winx = w;
       pwx = load_window(w);
     }
@@ -235,7 +281,7 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
   const int n_pro = min(kRing, total);
   for (int j = 0; j < n_pro; ++j) {
     const int w = window_for(j);
-    issue(j, j, pick_window(w, pw0, pw1, pwx));
+    issue(j, j, pick_window(w, pw0, pw1, pw2, pw3, pwx));
   }
 
   float Ms = -INFINITY, Ls = 0.0f, Os[64];
@@ -267,7 +313,7 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // K slot read: refill it
     if (2 * s + kRing < total) {
       const int w = window_for(2 * s + kRing);
-      issue(2 * s + kRing, sk, pick_window(w, pw0, pw1, pwx));
+      issue(2 * s + kRing, sk, pick_window(w, pw0, pw1, pw2, pw3, pwx));
     }
     // ---- softmax statistics of the sub-tile (log2 domain)
     // score v of the lane is key kk = 8(v/4) + 4g + v%4 of the sub-tile; it
@@ -352,18 +398,28 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // V slot read: refill it
     if (2 * s + 1 + kRing < total) {
       const int w = window_for(2 * s + 1 + kRing);
-      issue(2 * s + 1 + kRing, sv, pick_window(w, pw0, pw1, pwx));
+      issue(2 * s + 1 + kRing, sv, pick_window(w, pw0, pw1, pw2, pw3, pwx));
     }
     sk = sk + 2 >= kRing ? sk + 2 - kRing : sk + 2;
     sv = sv + 2 >= kRing ? sv + 2 - kRing : sv + 2;
-    // ---- end of a chunk: fold its partial into the segment result (ascending)
+    // ---- end of a chunk: fold its partial into the segment result
+    // (ascending), or, in a later part of a split segment, write it out
     if ((s + 1) % kSubsPerChunk == 0 || s + 1 == nsub) {
       float o[64];
 #pragma unroll
       for (int d = 0; d < 4; ++d)
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[16 * d + v] = oc[d][v];
-      fold_into<64>(Ms, Ls, Os, mc, lc, o);
+      if constexpr (kParts) {
+        if (first_part) {
+          fold_into<64>(Ms, Ls, Os, mc, lc, o);
+        } else {
+          const int64_t chunk = ((int64_t)v * Hkv + kvh) * nseg_max * (seg_tokens / kChunk) + sub_base / kChunk;
+          store_partial(ws.chunk_o, ws.chunk_ml, chunk, lane, mc, lc, o);
+        }
+      } else {
+        fold_into<64>(Ms, Ls, Os, mc, lc, o);
+      }
       mc = -INFINITY;
       lc = 0.0f;
 #pragma unroll
@@ -373,8 +429,9 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
     }
   }
 
+  if (!first_part) return;  // its chunk partials are out
   // value k = 16d + v of lane (li, g): dim 32d + 8(v/4) + 4g + v%4 of row li
-  if (nseg == 1) {
+  if (nseg == 1 && !split) {
     if (!row_ok) return;
     const float inv = Ls > 0.0f ? __fdiv_rn(1.0f, Ls) : 0.0f;
     uint16_t* orow = out + (qtok * Hq + hq) * kHD;
@@ -389,16 +446,9 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
     }
     return;
   }
-  // segment result -> workspace; attn_combine_kernel folds the segments
-  const int64_t slot = ((int64_t)v * Hkv + kvh) * nseg_max + seg;
-  float* slot_o = ws.part_o + slot * 4096;
-#pragma unroll
-  for (int qg = 0; qg < 16; ++qg) {  // one 1 KiB streaming store per group of four values
-    const f32x4 w = {Os[4 * qg + 0], Os[4 * qg + 1], Os[4 * qg + 2], Os[4 * qg + 3]};
-    __builtin_nontemporal_store(w, reinterpret_cast<f32x4*>(slot_o + (qg * 64 + lane) * 4));
-  }
-  ws.part_ml[slot * 128 + lane * 2 + 0] = Ms;
-  ws.part_ml[slot * 128 + lane * 2 + 1] = Ls;
+  // the segment result (or, for a split segment, the fold of its first
+  // part's chunks) -> workspace; attn_combine_kernel folds on from there
+  store_partial(ws.part_o, ws.part_ml, ((int64_t)v * Hkv + kvh) * nseg_max + seg, lane, Ms, Ls, Os);
 }
 
 // Work list for large grids: every full segment first, then the partial last
@@ -458,6 +508,42 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(const int32_t* __restri
   for (int i = n_items + tid; i < Rv * nseg_max; i += 1024) items[i] = -1;
 }
 
+// Parts per segment: halve the parts' length while the grid of segments
+// holds fewer than kSplitBelow potential waves (half a round of resident
+// waves on a 256-CU device), down to one 256-token chunk per part.  From the
+// call's shape alone.
+constexpr int64_t kSplitBelow = 512;
+static int attn_parts(int64_t Rv, int Hkv, int64_t nseg_max, int seg_tokens) {
+  const int cps = seg_tokens / kChunk;
+  const int64_t potential = Rv * Hkv * nseg_max;
+  int w = 1;
+  while (cps % (2 * w) == 0 && potential * w < kSplitBelow) w *= 2;
+  return w;
+}
+
+// Workspace: segment partials [Rv * Hkv * nseg_max] (4096 values + 128 for
+// (m, l) each), the work list (Rv * nseg_max entries, padded to 4), then,
+// when segments are split, the chunk partials [Rv * Hkv * nseg_max * chunks
+// per segment] in the same format.
+static size_t attn_ws_floats(int64_t Rv, int Hkv, int64_t nseg_max, int seg_tokens, int parts) {
+  const int64_t slots = Rv * Hkv * nseg_max;
+  const int64_t items = (Rv * nseg_max + 3) / 4 * 4;
+  const int64_t cslots = parts > 1 ? slots * (seg_tokens / kChunk) : 0;
+  return (size_t)(slots * (4096 + 128) + items + cslots * (4096 + 128));
+}
+static int32_t* attn_ws_items(void* workspace, int64_t Rv, int Hkv, int64_t nseg_max) {
+  return reinterpret_cast<int32_t*>(static_cast<float*>(workspace) + Rv * Hkv * nseg_max * (4096 + 128));
+}
+static AttnWs attn_ws_layout(void* workspace, int64_t Rv, int Hkv, int64_t nseg_max, int seg_tokens, int parts) {
+  const int64_t slots = Rv * Hkv * nseg_max;
+  AttnWs ws;
+  ws.part_o = static_cast<float*>(workspace);
+  ws.part_ml = ws.part_o + slots * 4096;
+  ws.chunk_o = ws.part_ml + slots * 128 + (Rv * nseg_max + 3) / 4 * 4;
+  ws.chunk_ml = ws.chunk_o + (parts > 1 ? slots * (seg_tokens / kChunk) * 4096 : 0);
+  return ws;
+}
+
 // Waves of the segment kernel resident at once on the current device (four
 // per CU: its LDS ring takes a quarter of a CU's 160 KiB).
 static int resident_attn_waves() {
@@ -472,25 +558,33 @@ static int resident_attn_waves() {
   return cached[dev];
 }
 
-// Second pass for requests with more than one segment: left-fold the segment
-// results in ascending order (the fold above, element by element) and write
-// the output.  One workgroup of 1024 threads per (KV head, request); thread t
-// takes lane t % 64 of the first pass and its values 4q .. 4q+3, q = t / 64
-// (dims 32(q/4) + 8(q%4) + 4g .. +3 of row (t%64) % 32).  Up to kCombBatch
-// segments are loaded at once, then folded in order.
-constexpr int kCombThreads = 1024, kCombBatch = 8;
+// Second pass for requests with more than one segment or a split segment:
+// per segment, in ascending order, its partial from the first pass and --
+// for a split segment -- the partials of its later chunks, folded on in
+// ascending order (completing the segment's left fold over its chunks);
+// then the segment results left-folded in ascending order from the first
+// one (the fold above, element by element), and the output written.  One
+// workgroup of 1024 threads per (KV head, row block); thread t takes lane
+// t % 64 of the first pass and its values 4q .. 4q+3, q = t / 64 (dims
+// 32(q/4) + 8(q%4) + 4g .. +3 of row (t%64) % 32).  Up to kCombBatch segment
+// partials, and kChunkBatch chunk partials, are loaded at once.
+constexpr int kCombThreads = 1024, kCombBatch = 8, kChunkBatch = 4;
 
 __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(const int32_t* __restrict__ ctx,
                                                                     uint16_t* __restrict__ out, int q_len, int Hq,
                                                                     int Hkv, int max_blocks, int seg_tokens,
-                                                                    int nseg_max, AttnWs ws, int blk_pos, int n_rb) {
+                                                                    int nseg_max, AttnWs ws, int blk_pos, int n_rb,
+                                                                    int parts) {
   const int kvh = blockIdx.x, v = blockIdx.y;  // v: row block, as in the first pass
   const int r = v / n_rb, j0 = (v - r * n_rb) * blk_pos;
   const int tid = threadIdx.x, q = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
   const int G = Hq / Hkv, jn = min(blk_pos, q_len - j0), nrows = jn * G;
   const int n_tok = min(ctx[r] + j0 + jn, max_blocks * 16);
   const int nseg = (n_tok + seg_tokens - 1) / seg_tokens;
-  if (nseg <= 1 || li >= nrows) return;  // single segment: written by the first pass
+  const int part_tok = seg_tokens / parts, cps = seg_tokens / kChunk, cpp = part_tok / kChunk;
+  // keys of segment s; it was split when they exceed one part
+  auto seg_keys = [&](int sg) { return min((sg + 1) * seg_tokens, n_tok) - sg * seg_tokens; };
+  if ((nseg <= 1 && seg_keys(0) <= part_tok) || li >= nrows) return;  // written by the first pass
   const int jq = j0 + li / G, hq = kvh * G + li % G;
   const int64_t slot0 = ((int64_t)v * Hkv + kvh) * nseg_max;
   float M = -INFINITY, Lt = 0.0f, O[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -508,8 +602,39 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(const int32_
       }
     }
 #pragma unroll
-    for (int b = 0; b < kCombBatch; ++b)
-      if (s0 + b < nseg) fold_into<4>(M, Lt, O, m[b], l[b], o[b]);
+    for (int b = 0; b < kCombBatch; ++b) {
+      const int sg = s0 + b;
+      if (sg >= nseg) continue;
+      const int keys = seg_keys(sg);
+      if (keys > part_tok) {  // split: the segment's chunks after its first part, loaded kChunkBatch at a time
+        const int nch = (keys + kChunk - 1) / kChunk;
+        for (int c0 = cpp; c0 < nch; c0 += kChunkBatch) {
+          float co[kChunkBatch][4], cm[kChunkBatch], cl[kChunkBatch];
+#pragma unroll
+          for (int e = 0; e < kChunkBatch; ++e) {
+            if (c0 + e < nch) {
+              const int64_t cs = slot0 * cps + (int64_t)sg * cps + c0 + e;
+              const f32x4 w = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ws.chunk_o + cs * 4096) + q * 64 + lane);
+#pragma unroll
+              for (int c = 0; c < 4; ++c) co[e][c] = w[c];
+              cm[e] = ws.chunk_ml[cs * 128 + lane * 2 + 0];
+              cl[e] = ws.chunk_ml[cs * 128 + lane * 2 + 1];
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < kChunkBatch; ++e)
+            if (c0 + e < nch) fold_into<4>(m[b], l[b], o[b], cm[e], cl[e], co[e]);
+        }
+      }
+      if (sg == 0) {
+        M = m[b];
+        Lt = l[b];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) O[c] = o[b][c];
+      } else {
+        fold_into<4>(M, Lt, O, m[b], l[b], o[b]);
+      }
+    }
   }
   const float inv = Lt > 0.0f ? __fdiv_rn(1.0f, Lt) : 0.0f;
   uint16_t* orow = out + (((int64_t)r * q_len + jq) * Hq + hq) * kHD + 32 * (q >> 2) + 8 * (q & 3) + 4 * g;
@@ -619,7 +744,7 @@ static inline int attn_row_blocks(int q_len, int Hq, int Hkv) { return (int)cdiv
 static biv_status launch_attn_bf16(const char* who, const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
                                    const int32_t* block_table, const int32_t* ctx, void* out, int R, int q_len,
                                    int Hq, int Hkv, int max_blocks, int num_blocks, float scale, int seg_tokens,
-                                   void* workspace, size_t workspace_bytes, hipStream_t s) {
+                                   bool allow_split, void* workspace, size_t workspace_bytes, hipStream_t s) {
   const int G = Hq / Hkv;
   BIV_REQUIRE(G >= 1 && 32 % G == 0, "%s: bf16 path needs Hq/Hkv dividing 32 (got %d)", who, G);
   const int blk_pos = attn_blk_pos(Hq, Hkv), n_rb = attn_row_blocks(q_len, Hq, Hkv);
@@ -633,30 +758,39 @@ static biv_status launch_attn_bf16(const char* who, const void* q, int64_t q_str
   BIV_REQUIRE(aligned16(workspace), "%s: workspace must be 16-byte aligned", who);
   const int nseg_max = (int)cdiv((int64_t)max_blocks * 16, seg_tokens);
   BIV_REQUIRE(nseg_max <= 0x7fffffff, "%s: too many segments", who);
-  AttnWs ws;
-  ws.part_o = static_cast<float*>(workspace);
-  ws.part_ml = ws.part_o + (size_t)Rv * Hkv * nseg_max * 4096;
+  // Segments split over several waves where the grid would otherwise hold
+  // few waves (decided by the call's shape alone; no bits change).
+  const int parts = allow_split ? attn_parts(Rv, Hkv, nseg_max, seg_tokens) : 1;
+  const AttnWs ws = attn_ws_layout(workspace, Rv, Hkv, nseg_max, seg_tokens, parts);
   // A grid of at least four rounds of resident waves is launched in LPT
   // order from a work list (decided by the call's shape alone).
-  const int64_t waves = (int64_t)Rv * nseg_max * Hkv;
+  const int64_t waves = (int64_t)Rv * nseg_max * Hkv * parts;
   int32_t* items = nullptr;
-  dim3 grid(nseg_max, Hkv, Rv);
-  if (waves >= 4 * (int64_t)resident_attn_waves() && waves <= 0x7fffffff) {
-    items = reinterpret_cast<int32_t*>(ws.part_ml + (size_t)Rv * Hkv * nseg_max * 128);
+  dim3 grid((unsigned)(nseg_max * parts), Hkv, Rv);
+  if (parts == 1 && waves >= 4 * (int64_t)resident_attn_waves() && waves <= 0x7fffffff) {
+    items = attn_ws_items(workspace, Rv, Hkv, nseg_max);
     hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, s, ctx, Rv, q_len, max_blocks, seg_tokens, nseg_max,
                        blk_pos, n_rb, items);
     biv_status st = launched(who);
     if (st != BIV_OK) return st;
     grid = dim3((unsigned)waves);
   }
-  hipLaunchKernelGGL(attn_bf16_kernel, grid, dim3(64), 0, s, static_cast<const uint16_t*>(q), q_stride,
-                     static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache), block_table, ctx,
-                     static_cast<uint16_t*>(out), q_len, Hq, Hkv, max_blocks, num_blocks, scale * kLog2e,
-                     seg_tokens, nseg_max, ws, items, blk_pos, n_rb);
+  // segments split over waves take the kernel with the chunk-partial path;
+  // the others a kernel without it (same arithmetic, leaner code)
+  if (parts > 1)
+    hipLaunchKernelGGL(attn_bf16_kernel<true>, grid, dim3(64), 0, s, static_cast<const uint16_t*>(q), q_stride,
+                       static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache), block_table, ctx,
+                       static_cast<uint16_t*>(out), q_len, Hq, Hkv, max_blocks, num_blocks, scale * kLog2e,
+                       seg_tokens, nseg_max, ws, items, blk_pos, n_rb, parts);
+  else
+    hipLaunchKernelGGL(attn_bf16_kernel<false>, grid, dim3(64), 0, s, static_cast<const uint16_t*>(q), q_stride,
+                       static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache), block_table, ctx,
+                       static_cast<uint16_t*>(out), q_len, Hq, Hkv, max_blocks, num_blocks, scale * kLog2e,
+                       seg_tokens, nseg_max, ws, items, blk_pos, n_rb, 1);
   biv_status st = launched(who);
-  if (st != BIV_OK || nseg_max <= 1) return st;
+  if (st != BIV_OK || (nseg_max <= 1 && parts == 1)) return st;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(Hkv, Rv), dim3(kCombThreads), 0, s, ctx, static_cast<uint16_t*>(out),
-                     q_len, Hq, Hkv, max_blocks, seg_tokens, nseg_max, ws, blk_pos, n_rb);
+                     q_len, Hq, Hkv, max_blocks, seg_tokens, nseg_max, ws, blk_pos, n_rb, parts);
   return launched(who);
 }
 
@@ -664,10 +798,9 @@ static biv_status launch_attn_bf16(const char* who, const void* q, int64_t q_str
 
 extern "C" size_t biv_attn_workspace_bytes(int R, int Hkv, int max_blocks, int seg_tokens) {
   using namespace biv;
-  if (R <= 0 || Hkv <= 0 || max_blocks <= 0 || seg_tokens <= 0) return 0;
-  const size_t nseg = (size_t)cdiv((int64_t)max_blocks * 16, seg_tokens);
-  // segment results, then the work list of large grids (R * nseg entries)
-  return (size_t)R * Hkv * nseg * (4096 + 128) * sizeof(float) + (size_t)R * nseg * sizeof(int32_t);
+  if (R <= 0 || Hkv <= 0 || max_blocks <= 0 || seg_tokens <= 0 || seg_tokens % kChunk != 0) return 0;
+  const int64_t nseg = cdiv((int64_t)max_blocks * 16, seg_tokens);
+  return attn_ws_floats(R, Hkv, nseg, seg_tokens, attn_parts(R, Hkv, nseg, seg_tokens)) * sizeof(float);
 }
 
 extern "C" size_t biv_attn_workspace_bytes_q(int R, int q_len, int Hq, int Hkv, int max_blocks, int seg_tokens) {
@@ -694,7 +827,7 @@ extern "C" biv_status attn_decode_bi(const void* q, int64_t q_stride, const void
     if (32 % (Hq / Hkv) != 0)
       return fail(BIV_EUNSUPPORTED, "attn_decode_bi: bf16 path needs Hq/Hkv dividing 32 (got %d)", Hq / Hkv);
     return launch_attn_bf16("attn_decode_bi", q, q_stride, k_cache, v_cache, block_table, ctx, out, R, q_len, Hq, Hkv,
-                            max_blocks, num_blocks, scale, BIV_ATTN_SEG_TOKENS, workspace, workspace_bytes, s);
+                            max_blocks, num_blocks, scale, BIV_ATTN_SEG_TOKENS, true, workspace, workspace_bytes, s);
   }
   if (D != 64 && D != 128) return fail(BIV_EUNSUPPORTED, "attn_decode_bi: fp32 path supports D in {64,128} (D=%d)", D);
   hipLaunchKernelGGL(attn_f32_kernel, dim3(q_len, Hq, R), dim3(64), 0, s, static_cast<const float*>(q), q_stride,
@@ -727,6 +860,6 @@ extern "C" biv_status attn_decode_adaptive(const void* q, int64_t q_stride, cons
   BIV_REQUIRE(split_tokens >= 0 && split_tokens % kChunk == 0, "attn_decode_adaptive: split_tokens must be a multiple of %d", kChunk);
   const int split = split_tokens == 0 ? biv_attn_adaptive_split(R, Hkv, max_blocks) : split_tokens;
   return launch_attn_bf16("attn_decode_adaptive", q, q_stride, k_cache, v_cache, block_table, ctx, out, R, q_len, Hq, Hkv,
-                          max_blocks, num_blocks, scale, split, workspace, workspace_bytes,
+                          max_blocks, num_blocks, scale, split, false, workspace, workspace_bytes,
                           static_cast<hipStream_t>(stream));
 }

@@ -645,9 +645,11 @@ def _attn_ref(lay, kc, vc, q, q_len, dtype="bf16"):
 @pytest.mark.parametrize("q_len", [1, 8])
 def test_attention_bf16_parity(biv, q_len):
     """32 q heads / 8 KV heads x 128, paged KV (16-token pages, permuted),
-    contexts spanning several 256-token chunks and 2048-token segments plus
-    ragged tails and exact boundaries."""
-    ctx = [0, 255 - q_len + 1, 256, 1023, 1024, 1025, 2048 - q_len, 2049 - q_len, 2500, 5000]
+    contexts spanning several 256-token chunks and 4096-token segments plus
+    ragged tails and exact boundaries (13 requests: segments split over
+    several waves)."""
+    ctx = [0, 255 - q_len + 1, 256, 1023, 1024, 1025, 2048 - q_len, 2049 - q_len, 2500, 4096 - q_len,
+           4097 - q_len, 5000, 9000]
     R = len(ctx)
     lay, kc, vc, q = _attn_inputs(R, q_len, 32, 8, 128, ctx, seed=50 + q_len)
     announce("attention bf16 parity q_len", q_len)
@@ -694,7 +696,7 @@ def test_attention_bf16_batch_invariance(biv):
 def test_attention_bf16_verify_rows_equal_single_decodes(biv):
     """Row j of a K=8 verify block equals, bit for bit, the same query decoded
     alone (K=1) at context L+j: extra masked keys and chunks fold as no-ops."""
-    q_len, Hq, Hkv, D, L = 8, 32, 8, 128, 1530  # crosses a chunk and a segment boundary
+    q_len, Hq, Hkv, D, L = 8, 32, 8, 128, 4090  # crosses a chunk and a segment boundary
     lay, kc, vc, q = _attn_inputs(1, q_len, Hq, Hkv, D, [L], seed=70)
     announce("attention verify vs decode")
     block = bits(_run_attn(biv, lay, kc, vc, q, q_len))
