@@ -71,14 +71,20 @@ struct AttnWs {
 };
 
 // Partial (m, l, o[64]) of a lane -> slot `slot` of (po, pml): sixteen 1 KiB
-// streaming stores of four values each, then m and l.
+// stores of four values each (streaming stores for segment partials; chunk
+// partials, few and read back soon, go through the caches), then m and l.
+template <bool kStream>
 __device__ __forceinline__ void store_partial(float* po, float* pml, int64_t slot, int lane, float m, float l,
                                               const float* o) {
   float* so = po + slot * 4096;
 #pragma unroll
   for (int qg = 0; qg < 16; ++qg) {
     const f32x4 w = {o[4 * qg + 0], o[4 * qg + 1], o[4 * qg + 2], o[4 * qg + 3]};
-    __builtin_nontemporal_store(w, reinterpret_cast<f32x4*>(so + (qg * 64 + lane) * 4));
+    f32x4* dst = reinterpret_cast<f32x4*>(so + (qg * 64 + lane) * 4);
+    if constexpr (kStream)
+      __builtin_nontemporal_store(w, dst);
+    else
+      *dst = w;
   }
   pml[slot * 128 + lane * 2 + 0] = m;
   pml[slot * 128 + lane * 2 + 1] = l;
@@ -415,7 +421,7 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
           fold_into<64>(Ms, Ls, Os, mc, lc, o);
         } else {
           const int64_t chunk = ((int64_t)v * Hkv + kvh) * nseg_max * (seg_tokens / kChunk) + sub_base / kChunk;
-          store_partial(ws.chunk_o, ws.chunk_ml, chunk, lane, mc, lc, o);
+          store_partial<false>(ws.chunk_o, ws.chunk_ml, chunk, lane, mc, lc, o);
         }
       } else {
         fold_into<64>(Ms, Ls, Os, mc, lc, o);
@@ -448,7 +454,7 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
   }
   // the segment result (or, for a split segment, the fold of its first
   // part's chunks) -> workspace; attn_combine_kernel folds on from there
-  store_partial(ws.part_o, ws.part_ml, ((int64_t)v * Hkv + kvh) * nseg_max + seg, lane, Ms, Ls, Os);
+  store_partial<true>(ws.part_o, ws.part_ml, ((int64_t)v * Hkv + kvh) * nseg_max + seg, lane, Ms, Ls, Os);
 }
 
 // Work list for large grids: every full segment first, then the partial last
@@ -614,7 +620,7 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(const int32_
           for (int e = 0; e < kChunkBatch; ++e) {
             if (c0 + e < nch) {
               const int64_t cs = slot0 * cps + (int64_t)sg * cps + c0 + e;
-              const f32x4 w = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ws.chunk_o + cs * 4096) + q * 64 + lane);
+              const f32x4 w = *(reinterpret_cast<const f32x4*>(ws.chunk_o + cs * 4096) + q * 64 + lane);
 #pragma unroll
               for (int c = 0; c < 4; ++c) co[e][c] = w[c];
               cm[e] = ws.chunk_ml[cs * 128 + lane * 2 + 0];
