@@ -11,7 +11,8 @@
 //   sub-tile = 32 keys (one MFMA block), chunk = 256 keys (the KV split),
 //   segment  = seg_tokens keys (4096 for the invariant kernel), taken by one
 //              wave, or split over several at small batch (see the kernel).
-// One 64-lane wave per (segment, KV head, row block), four per CU.  The rows
+// One 64-lane wave per (segment, KV head, row block) -- or per part of a
+// segment where the grid holds few segments -- four per CU.  The rows
 // of one KV head in a row block (32/G positions x G query heads) share one
 // 32-row MFMA block, so the K/V of a page is read once for all of them (the
 // pages' tile rule: G x (1+D) rows per KV head, here G x K <= 32: a verify
@@ -21,12 +22,14 @@
 // (gfx950 global_load_lds_dwordx4) and computes S^T = K Q^T and O^T = V^T P^T
 // on the 32x32x16 bf16 MFMA, softmax statistics in fp32 (log2 domain),
 // sub-tile by sub-tile in ascending order; each finished chunk's partial
-// (m, l, o) is left-folded into the segment result in registers.  Segment
-// results go to the workspace; a second, small kernel left-folds them in
-// ascending order and writes the output (a request with a single segment is
+// (m, l, o) is left-folded into the segment result in registers (in the
+// later parts of a split segment it is stored instead).  Segment results
+// (and stored chunk partials) go to the workspace; a second, small kernel
+// completes split segments' folds, left-folds the segments in ascending
+// order and writes the output (a request with a single, unsplit segment is
 // written directly).  A kernel boundary, not a device-wide fence, makes the
-// segment results visible: on gfx950 such a fence writes back and
-// invalidates the whole L2 of an XCD.
+// partials visible: on gfx950 such a fence writes back and invalidates the
+// whole L2 of an XCD.
 //
 // Every boundary is an absolute position and every fold runs in ascending
 // order, so a row's bits depend only on its own query, its own request's KV
