@@ -1,0 +1,185 @@
+"""The verifier step at the full width of the Llama-3-8B-shaped pass, in the
+launch configuration the benchmark times: 64 requests x K = 8 candidates
+(W = 512 rows), contexts U[2048, 8192] on 16-token pages placed by a seeded
+permutation, hidden 4096, 32/8 heads x 128, FFN 14336, vocab 128256, bf16,
+the same seeds as the benchmark's pass, and the step captured as one HIP
+graph with the lm_head matmul and the Gumbel verification fused.  Two of the
+32 layers are built: the layer count changes no launch (every kernel sees
+the pass's own grid), only how many times it runs.
+
+LLM-42 post, paragraphs 3-4 (verify K candidates of each of N requests in
+one forward, overwrite the fast path's KV) and the Gumbel post (Gumbel-max
+verification with prepared noise).
+
+The oracle cannot take all 64 requests at this width in seconds, so it checks
+sampled requests one by one -- the longest context, the shortest and six
+seeded others -- on host copies of their own pages:
+  * logits of their rows within the bf16 pass's bound of the fp64 oracle;
+  * targets equal the oracle's Gumbel-max decisions on every row whose top-2
+    margin is clear of the logit error (rows nearer a tie are counted);
+  * planted first divergences are recovered exactly (accept_len == d) and
+    the corrections are the target tokens at d;
+  * the graph replay with the fused head gives the eager step's targets,
+    accepted lengths and corrections bit for bit;
+  * a sampled request verified alone gives its rows' logits bit for bit as
+    inside the 64-request batch (batch invariance at full width).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from gpu_util import DEV, announce, bits, f64, sync
+
+pytestmark = pytest.mark.gpu
+
+N_REQ, K, CTX_LO, CTX_HI = 64, 8, 2048, 8192
+LAYERS = 2
+# The bf16 pass's logits bound against fp64, the one the two-layer slice of
+# the same shape uses (bf16 storage of activations between the kernels).
+LOGIT_ABS = 0.25
+
+
+class _EmbedRows:
+    """fp64 rows of the device embedding, gathered on demand (the oracle
+    only indexes it by token ids); saves a 4 GB fp64 copy of the table."""
+
+    def __init__(self, table):
+        self.table = table
+
+    def __getitem__(self, ids):
+        idx = torch.from_numpy(np.asarray(ids, dtype=np.int64)).to(DEV)
+        return f64(self.table[idx])
+
+
+@pytest.fixture(scope="module")
+def V():
+    import invariant_verify_verifier_amd.verifier as verifier
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return verifier
+
+
+@pytest.fixture(scope="module")
+def world(V):
+    sh = wl.LLAMA3_8B
+    ctx = wl.context_lengths(wl.SEEDS["pass_len"], N_REQ, CTX_LO, CTX_HI)
+    lay = wl.paged_layout(ctx, K, seed=wl.SEEDS["pass_len"] + 1)
+    announce("full-width pass setup", N_REQ, "requests,", lay.num_blocks, "pages")
+    dw = wl.device_model_weights(sh, wl.SEEDS["pass_weights"], layers=LAYERS)
+    caches = wl.device_kv_cache(sh, lay.num_blocks, wl.SEEDS["pass_kv"], layers=LAYERS)
+    shape = V.Shape(LAYERS, sh.hidden, sh.heads, sh.kv_heads, sh.head_dim, sh.ffn, sh.vocab, sh.eps, sh.rope_theta)
+    model = V.VerifierModel(shape, torch.bfloat16, dw["layers"], dw["embed"], dw["lm_head"], dw["final_norm"],
+                            max_pos=16384)
+    t0 = wl.tokens(wl.SEEDS["pass_tokens"], (N_REQ,), sh.vocab)
+    cand0 = wl.tokens(wl.SEEDS["pass_tokens"] + 1, (N_REQ, K), sh.vocab)
+    pos = ctx[:, None] + np.arange(K)[None, :] + 1
+    noise = wl.gumbel_noise(wl.SEEDS["pass_noise"], np.repeat(np.arange(N_REQ), K).reshape(N_REQ, K), pos,
+                            sh.vocab)
+    announce("full-width pass self-consistent candidates")
+    tgt = V.self_consistent_candidates(model, t0, ctx, lay.block_table, noise, caches, K, first=cand0)
+    d = wl.rng(wl.SEEDS["pass_tokens"] + 2).integers(0, K + 1, size=N_REQ)
+    cand = wl.plant_divergence(tgt, d, sh.vocab, wl.SEEDS["pass_tokens"] + 2)
+    batch = V.make_batch(t0, cand, ctx, lay.block_table, noise)
+    yield dict(sh=sh, ctx=ctx, lay=lay, dw=dw, caches=caches, model=model, batch=batch, d=d, t0=t0, cand=cand,
+               noise=noise, tgt=tgt)
+    del model, caches, dw
+    torch.cuda.empty_cache()
+
+
+def _oracle_weights(sh, dw):
+    H, D, F = sh.hidden, sh.head_dim, sh.ffn
+    q, kv = sh.heads * D, sh.kv_heads * D
+    d = dict(shape=wl.ModelShape(LAYERS, H, sh.heads, sh.kv_heads, D, F, sh.vocab, sh.eps, sh.rope_theta),
+             embed=_EmbedRows(dw["embed"]), lm_head=f64(dw["lm_head"]), final_norm=f64(dw["final_norm"]),
+             layers=[])
+    for L in dw["layers"]:
+        wqkv, wgu = f64(L["wqkv"]), f64(L["w_gu"])
+        d["layers"].append(dict(attn_norm=f64(L["attn_norm"]), wq=wqkv[:q], wk=wqkv[q:q + kv], wv=wqkv[q + kv:],
+                                wo=f64(L["wo"]), ffn_norm=f64(L["ffn_norm"]), w_gate=wgu[:F], w_up=wgu[F:],
+                                w_down=f64(L["w_down"])))
+    return d
+
+
+def _oracle_request(ow, world, r):
+    """Oracle logits [K, V] of request r, from host copies of its own pages
+    (the context positions are never written by the step; the candidate
+    slots are written by the oracle itself before its attention reads them)."""
+    lay, caches = world["lay"], world["caches"]
+    pages = [int(p) for p in lay.block_table[r] if p >= 0]
+    idx = torch.tensor(pages, device=DEV)
+    okc = [f64(kc[idx]) for kc, _ in caches]
+    ovc = [f64(vc[idx]) for _, vc in caches]
+    bt = np.full((1, lay.block_table.shape[1]), -1, np.int32)
+    bt[0, :len(pages)] = np.arange(len(pages))
+    toks = np.concatenate([world["t0"][r:r + 1], world["cand"][r, :K - 1]])[None, :]
+    return oracle.decoder_forward(ow, toks, world["ctx"][r:r + 1], okc, ovc, bt)
+
+
+def _sampled(ctx):
+    g = wl.rng(wl.SEEDS["pass_tokens"] + 30)
+    picks = [int(np.argmax(ctx)), int(np.argmin(ctx))]
+    for r in g.permutation(len(ctx)):
+        if int(r) not in picks:
+            picks.append(int(r))
+        if len(picks) == 8:
+            break
+    return picks
+
+
+def test_full_width_pass_sampled_parity_planted_graph_and_invariance(V, world):
+    model, batch, caches = world["model"], world["batch"], world["caches"]
+    d, tgt, noise = world["d"], world["tgt"], world["noise"]
+    announce("full-width pass eager step")
+    logits, e_tgt, e_acc, e_nxt = model.verify(batch, caches)
+    sync()
+    g_logits = f64(logits).reshape(N_REQ, K, -1)
+    g_bits = bits(logits).reshape(N_REQ, K, -1).copy()
+    e_tgt, e_acc, e_nxt = e_tgt.cpu().numpy(), e_acc.cpu().numpy(), e_nxt.cpu().numpy()
+
+    # planted first divergences, recovered exactly
+    assert np.array_equal(e_acc, d)
+    for r in range(N_REQ):
+        assert e_nxt[r] == (tgt[r, d[r]] if d[r] < K else -1), r
+
+    # the benchmark's launch: one HIP graph, fused lm_head + Gumbel verify
+    announce("full-width pass graph capture (fused head)")
+    graph = model.capture(batch, caches, fused_head=True)
+    for i in range(2):
+        for t in (batch.target, batch.accept_len, batch.next_token):
+            t.fill_(-7)
+        sync()
+        announce("full-width pass graph replay", i)
+        graph.replay()
+        sync()
+        assert np.array_equal(batch.target.cpu().numpy(), e_tgt), f"replay {i}: target"
+        assert np.array_equal(batch.accept_len.cpu().numpy(), e_acc), f"replay {i}: accept_len"
+        assert np.array_equal(batch.next_token.cpu().numpy(), e_nxt), f"replay {i}: next_token"
+    del graph
+
+    # sampled requests against the fp64 oracle
+    ow = _oracle_weights(world["sh"], world["dw"])
+    picks = _sampled(world["ctx"])
+    near = 0
+    for r in picks:
+        announce("full-width pass oracle, request", r, "context", int(world["ctx"][r]))
+        olog = _oracle_request(ow, world, r)
+        err = np.abs(g_logits[r] - olog)
+        print(f"request {r} (context {world['ctx'][r]}): logits max abs err {err.max():.4f}, "
+              f"|ref| max {np.abs(olog).max():.2f}")
+        assert err.max() <= LOGIT_ABS, r
+        s = oracle.perturbed_scores(olog.astype(np.float32)[None], noise[r:r + 1])[0]
+        srt = np.sort(s, axis=-1)
+        safe = (srt[:, -1] - srt[:, -2]) > 4 * err.max()
+        near += int((~safe).sum())
+        assert np.array_equal(e_tgt[r][safe], np.argmax(s, axis=-1)[safe]), r
+    print(f"{near} of {len(picks) * K} sampled rows within 4x the logit error of a tie")
+
+    # batch invariance at full width: a request alone = its rows in the batch
+    for r in picks[:3]:
+        announce("full-width pass request alone", r)
+        bb = V.make_batch(world["t0"][[r]], world["cand"][[r]], world["ctx"][[r]], world["lay"].block_table[[r]],
+                          noise[[r]])
+        one = bits(model.verify(bb, caches)[0]).reshape(1, K, -1)
+        assert np.array_equal(one[0], g_bits[r]), r
