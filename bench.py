@@ -321,6 +321,46 @@ def time_graph(torch, model, batch, caches, steps, warmup, **kw):
     return start.elapsed_time(end) / steps
 
 
+def gpu_state_under_load(torch, replay, limit_s=20):
+    """rocm-smi's clocks, socket power and performance level, read while the
+    pass replays (untimed, after the timed region); None where the tool is
+    missing or fails."""
+    import shutil
+    import subprocess
+    import threading
+
+    tool = shutil.which("rocm-smi")
+    if tool is None:
+        return None
+    out = {}
+
+    def sample():
+        try:
+            p = subprocess.run([tool, "--showclocks", "--showpower", "--showperflevel", "--json"],
+                               capture_output=True, text=True, timeout=limit_s)
+            out["text"] = p.stdout
+        except (OSError, subprocess.SubprocessError) as e:
+            out["error"] = repr(e)
+
+    th = threading.Thread(target=sample)
+    th.start()
+    while th.is_alive():  # the tool's own time limit ends this loop
+        replay()
+        torch.cuda.synchronize()
+    th.join()
+    try:
+        cards = json.loads(out.get("text", ""))
+    except ValueError:
+        return {"error": out.get("error", "unparsed rocm-smi output")}
+    keep = {}
+    for card, fields in cards.items():
+        if isinstance(fields, dict):
+            keep[card] = {k.strip(" :"): v for k, v in fields.items()
+                          if any(w in k.lower() for w in ("clk", "power", "performance"))}
+    return {"tool": "rocm-smi --showclocks --showpower --showperflevel", "sampled": "during untimed graph replays",
+            "cards": keep}
+
+
 def time_passes(torch, model, batch, caches, steps, **kw):
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -838,6 +878,7 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(end) / args.steps
     assert np.array_equal(batch.accept_len.cpu().numpy(), acc_bi), "graph replay changed decisions"
+    gpu_state = gpu_state_under_load(torch, graph.replay)
     del graph
     W = N_REQ * K_CAND
     # the same pass with split-K GEMMs and load-adaptive attention splits
@@ -890,6 +931,7 @@ def main():
                      "bytes_per_launch": attn_bytes, "avg_launch_ms": round(attn_ms, 5),
                      "launches_timed": len(timer.pairs)},
         "cpu_baseline": None,
+        "gpu_state": gpu_state,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
