@@ -549,9 +549,60 @@ static void launch_dma_t(const void* A, const void* B, void* C, float* partial, 
                      tilesM, tilesN, k_per_split);
 }
 
+// Few rows (M <= 64, decode-sized batches): the same tiling of N (tile
+// width, waves along N, hence the same workgroup per output column block)
+// and the same per-element reduction, with the tile's rows cut to 32 or 64.
+// No copies are spent on rows past M (a 128-row tile at M = 1 copies 128
+// activation rows per stage for one useful row), and the LDS this frees holds
+// a deeper ring of weight stages: small-M calls stream the weight, so the
+// weight bytes in flight per CU set their speed.  Rows, stages, waves along
+// M, for the tile classes above:
+#define BIV_GEMM_L32_TILE 32, 256, 4, 1, 4   // 144 KiB, three weight stages in flight
+#define BIV_GEMM_L64_TILE 64, 256, 3, 2, 4   // 120 KiB
+#define BIV_GEMM_N32_TILE 32, 64, 8, 1, 2    // S and T classes: 96 KiB, seven stages in flight
+#define BIV_GEMM_N64_TILE 64, 64, 8, 2, 2    // 128 KiB
+#define BIV_GEMM_Q32_TILE 32, 96, 3, 1, 1    // 128-wide k: 96 KiB
+#define BIV_GEMM_Q64R_TILE 64, 96, 3, 2, 1   // 128-wide k: 120 KiB
+#define BIV_GEMM_Q32K64_TILE 32, 96, 5, 1, 1  // 64-wide k: 80 KiB
+#define BIV_GEMM_Q64K64_TILE 64, 96, 4, 2, 1  // 64-wide k: 80 KiB
+constexpr int kSmallRows = 64;
+static_assert(wave_cols<BIV_GEMM_L32_TILE>() == kGumbelGroup && wave_cols<BIV_GEMM_L64_TILE>() == kGumbelGroup,
+              "the Gumbel epilogue's group width is the L tile's columns per wave at every row count");
+
+template <int OUT_DT, int EPI>
+static void launch_dma_small(DmaTile t, const void* A, const void* B, void* C, float* partial, int M, int N, int K,
+                             hipStream_t s) {
+  const bool r32 = M <= 32;
+  if constexpr (EPI == BIV_EPI_SWIGLU || EPI == kEpiGumbel) {  // these epilogues run the L tile only
+    (void)t;
+    if (r32) launch_dma_t<BIV_GEMM_L32_TILE, OUT_DT, EPI, false>(A, B, C, partial, M, N, K, 1, K, s);
+    else launch_dma_t<BIV_GEMM_L64_TILE, OUT_DT, EPI, false>(A, B, C, partial, M, N, K, 1, K, s);
+  } else if (t == kTileL) {
+    if (r32) launch_dma_t<BIV_GEMM_L32_TILE, OUT_DT, EPI, false>(A, B, C, partial, M, N, K, 1, K, s);
+    else launch_dma_t<BIV_GEMM_L64_TILE, OUT_DT, EPI, false>(A, B, C, partial, M, N, K, 1, K, s);
+  } else if (t == kTileQ) {
+    if (K % 128 == 0) {
+      if (r32) launch_dma_t<BIV_GEMM_Q32_TILE, OUT_DT, EPI, false, 128>(A, B, C, partial, M, N, K, 1, K, s);
+      else launch_dma_t<BIV_GEMM_Q64R_TILE, OUT_DT, EPI, false, 128>(A, B, C, partial, M, N, K, 1, K, s);
+    } else {
+      if (r32) launch_dma_t<BIV_GEMM_Q32K64_TILE, OUT_DT, EPI, false>(A, B, C, partial, M, N, K, 1, K, s);
+      else launch_dma_t<BIV_GEMM_Q64K64_TILE, OUT_DT, EPI, false>(A, B, C, partial, M, N, K, 1, K, s);
+    }
+  } else {  // S and T: 64 columns, two waves along N
+    if (r32) launch_dma_t<BIV_GEMM_N32_TILE, OUT_DT, EPI, false>(A, B, C, partial, M, N, K, 1, K, s);
+    else launch_dma_t<BIV_GEMM_N64_TILE, OUT_DT, EPI, false>(A, B, C, partial, M, N, K, 1, K, s);
+  }
+}
+
 template <int OUT_DT, int EPI, bool kSplit>
 static void launch_dma(DmaTile t, const void* A, const void* B, void* C, float* partial, int M, int N, int K,
                        int splits, int k_per_split, hipStream_t s) {
+  if constexpr (!kSplit) {
+    if (M <= kSmallRows) {
+      launch_dma_small<OUT_DT, EPI>(t, A, B, C, partial, M, N, K, s);
+      return;
+    }
+  }
   if (t == kTileL)
     launch_dma_t<BIV_GEMM_L_TILE, OUT_DT, EPI, kSplit>(A, B, C, partial, M, N, K, splits, k_per_split, s);
   else if (t == kTileS)
@@ -602,10 +653,14 @@ extern "C" biv_status gemm_bi(const void* A, const void* B, void* C, int64_t M, 
     BIV_REQUIRE((int64_t)K * 2 * 16 <= 0x7fffffff, "gemm_bi: K too large");
     // the wide tile for every N: its waves hold two 32-column fragments, a
     // gate block and the matching up block
-    if (out_dt == BIV_BF16)
+    if (m <= kSmallRows) {
+      if (out_dt == BIV_BF16) launch_dma_small<BIV_BF16, BIV_EPI_SWIGLU>(kTileL, A, B, C, nullptr, m, n, k, s);
+      else launch_dma_small<BIV_F32, BIV_EPI_SWIGLU>(kTileL, A, B, C, nullptr, m, n, k, s);
+    } else if (out_dt == BIV_BF16) {
       launch_dma_t<BIV_GEMM_L_TILE, BIV_BF16, BIV_EPI_SWIGLU, false>(A, B, C, nullptr, m, n, k, 1, k, s);
-    else
+    } else {
       launch_dma_t<BIV_GEMM_L_TILE, BIV_F32, BIV_EPI_SWIGLU, false>(A, B, C, nullptr, m, n, k, 1, k, s);
+    }
     return launched("gemm_bi/bf16-swiglu");
   }
   if (in_dt == BIV_BF16) {
@@ -730,8 +785,12 @@ extern "C" biv_status lm_head_gumbel_verify(const void* h, const void* w_head, c
   BIV_REQUIRE(workspace_bytes >= biv_gumbel_workspace_bytes(M, V),
               "lm_head_gumbel_verify: workspace %zu < %zu bytes", workspace_bytes, biv_gumbel_workspace_bytes(M, V));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  launch_dma_t<BIV_GEMM_L_TILE, BIV_F32, kEpiGumbel, false>(h, w_head, const_cast<float*>(noise),
-                                                           static_cast<float*>(workspace), M, V, H, 1, H, s);
+  if (M <= kSmallRows)
+    launch_dma_small<BIV_F32, kEpiGumbel>(kTileL, h, w_head, const_cast<float*>(noise), static_cast<float*>(workspace),
+                                          M, V, H, s);
+  else
+    launch_dma_t<BIV_GEMM_L_TILE, BIV_F32, kEpiGumbel, false>(h, w_head, const_cast<float*>(noise),
+                                                             static_cast<float*>(workspace), M, V, H, 1, H, s);
   const biv_status st = launched("lm_head_gumbel_verify/gemm");
   if (st != BIV_OK) return st;
   return launch_gumbel_finish(static_cast<const uint2*>(workspace), (V + kGumbelGroup - 1) / kGumbelGroup, cand, R, K, target,
