@@ -166,7 +166,7 @@ def test_gumbel_topk_bitwise(biv, rows, V, k):
 # =====================================================================
 
 
-@pytest.mark.parametrize("R,K,V", [(5, 8, 128256), (3, 3, 50021)])
+@pytest.mark.parametrize("R,K,V", [(5, 8, 128256), (3, 3, 50021), (12, 8, 50021)])
 def test_lm_head_gumbel_verify_bitwise(biv, R, K, V):
     """The fused call gives the bits of gemm_bi (fp32 logits) + gumbel_verify,
     and both equal the oracle's rule applied to the GPU's logits.  Planted in
@@ -494,12 +494,14 @@ def test_gemm_swiglu_epilogue_ragged_and_unfused_layout(biv):
     check_f32(f64(c2), ref, axis=1, what="swiglu unfused over the packed weight")
 
 
-@pytest.mark.parametrize("N", [4096, 6144, 6184, 28672])
+@pytest.mark.parametrize("N", [4096, 6144, 6184, 14336, 28672])
 def test_gemm_bf16_tile_classes_invariance(biv, N):
-    """Each weight-width class of the staged kernel (its own tile: N <= 4096,
-    4096 < N < 8192 with 6184 ragged against the tile, N >= 16384), K = 4096:
-    parity with the oracle at M = 333 (ragged rows), and every row's bits the
-    same for M = 1, 7, 64, 333 as inside M = 512."""
+    """Each weight-width class of the staged kernel (its own column tiling:
+    N <= 4096, 4096 < N < 8192 with 6184 ragged against the tile,
+    8192 <= N < 16384, N >= 16384), K = 4096: parity with the oracle at
+    M = 333 (ragged rows), and every row's bits the same for M = 1, 7, 32, 33,
+    64, 65, 333 as inside M = 512 -- across the 32-row (M <= 32), 64-row
+    (M <= 64) and full-height tiles."""
     K = 4096
     a_np = wl.normal_bf16(130, (512, K))
     w_np = wl.normal_bf16(131 + N % 7, (N, K), std=0.02)
@@ -511,7 +513,7 @@ def test_gemm_bf16_tile_classes_invariance(biv, N):
     full_bits = bits(full)
     ref = oracle.linear(oracle.as_f64(a_np[:333], "bf16"), oracle.as_f64(w_np, "bf16"))
     check_f32(f64(full)[:333], ref, axis=1, what=f"gemm N={N}")
-    for M in (1, 7, 64, 333):
+    for M in (1, 7, 32, 33, 64, 65, 333):
         cM = torch.empty((M, N), dtype=torch.float32, device=DEV)
         biv.gemm_bi(a[:M].contiguous(), w, cM)
         sync()
@@ -524,7 +526,8 @@ def test_gemm_bf16_tiles_and_k_widths_change_no_bits(biv, K):
     when K % 128 == 0, else 64-wide) against its column slices of 4096 and
     2048 rows (the 128 x 64 tile, 64-wide k stages): every output element is
     reduced in the same order whatever tile and k width hold it, so the
-    columns agree bit for bit (fp32 and bf16 outputs)."""
+    columns agree bit for bit (fp32 and bf16 outputs); the same rows at
+    M = 5 and 40 (32- and 64-row tiles) match too."""
     M, N = 333, 6144
     a_np = wl.normal_bf16(140, (M, K))
     w_np = wl.normal_bf16(141, (N, K), std=0.02)
@@ -541,6 +544,11 @@ def test_gemm_bf16_tiles_and_k_widths_change_no_bits(biv, K):
         fb = bits(full)
         assert np.array_equal(bits(lo), fb[:, :4096]), f"K={K} {dt}: columns 0..4095"
         assert np.array_equal(bits(hi), fb[:, 4096:]), f"K={K} {dt}: columns 4096.."
+        for m in (5, 40):  # the 32- and 64-row tiles of both classes, both k widths
+            part = torch.empty((m, N), dtype=dt, device=DEV)
+            biv.gemm_bi(a[:m].contiguous(), w, part)
+            sync()
+            assert np.array_equal(bits(part), fb[:m]), f"K={K} {dt}: rows changed at M={m}"
     ref = oracle.linear(oracle.as_f64(a_np, "bf16"), oracle.as_f64(w_np, "bf16"))
     check_bf16(f64(full), ref, f"gemm tiles K={K}")
 
