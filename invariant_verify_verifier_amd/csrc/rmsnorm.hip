@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const void* __res
 }
 
 // Vector path for H = 1024 * NV: lane t holds elements 4t + 1024j .. +3,
-// j = 0..NV-1, read once.
+// j = 0..NV-1, and the same elements of gamma, read once.
 template <int XDT, int YDT, int NV>
 __global__ __launch_bounds__(kNormThreads) void rmsnorm_vec_kernel(const void* __restrict__ x,
                                                                    const void* __restrict__ gamma,
@@ -68,6 +68,23 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_vec_kernel(const void* _
       v[j][3] = bf2f((uint16_t)(q.y >> 16));
     }
   }
+  // gamma is loaded with x, so its latency hides behind the reduction
+  float gm[NV][4];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int i0 = 4 * t + 1024 * j;
+    if constexpr (YDT == BIV_F32) {
+      const f32x4 q = *reinterpret_cast<const f32x4*>(static_cast<const float*>(gamma) + i0);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) gm[j][c] = q[c];
+    } else {
+      const uint2 q = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(gamma) + i0);
+      gm[j][0] = bf2f((uint16_t)(q.x & 0xffffu));
+      gm[j][1] = bf2f((uint16_t)(q.x >> 16));
+      gm[j][2] = bf2f((uint16_t)(q.y & 0xffffu));
+      gm[j][3] = bf2f((uint16_t)(q.y >> 16));
+    }
+  }
   float ss = 0.0f;
 #pragma unroll
   for (int j = 0; j < NV; ++j)
@@ -87,7 +104,7 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_vec_kernel(const void* _
     const int i0 = 4 * t + 1024 * j;
     float o[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) o[c] = __fmul_rn(__fmul_rn(v[j][c], inv), load_as_f32(gamma, i0 + c, YDT));
+    for (int c = 0; c < 4; ++c) o[c] = __fmul_rn(__fmul_rn(v[j][c], inv), gm[j][c]);
     if constexpr (YDT == BIV_F32) {
       const f32x4 q = {o[0], o[1], o[2], o[3]};
       *reinterpret_cast<f32x4*>(static_cast<float*>(y) + base + i0) = q;
@@ -129,7 +146,8 @@ extern "C" biv_status rmsnorm_bi(const void* x, biv_dtype x_dt, const void* gamm
   hipStream_t s = static_cast<hipStream_t>(stream);
   // vector path: H of 1024, 2048, 4096 or 8192 and 16-byte aligned rows (the
   // path is fixed by H and the pointers, never by M)
-  const bool vec = (H == 1024 || H == 2048 || H == 4096 || H == 8192) && aligned16(x) && aligned16(y);
+  const bool vec = (H == 1024 || H == 2048 || H == 4096 || H == 8192) && aligned16(x) && aligned16(y) &&
+                   aligned16(gamma);
   if (x_dt == BIV_F32 && y_dt == BIV_F32)
     launch_norm<BIV_F32, BIV_F32>(x, gamma, y, M, H, eps, s, vec);
   else if (x_dt == BIV_F32 && y_dt == BIV_BF16)
