@@ -61,6 +61,34 @@ __global__ void embed_rows_kernel(const int32_t* __restrict__ ids, const void* _
   }
 }
 
+// bf16 table, 16-byte pieces: one thread per 8 elements of a row (the same
+// values as the element loop: bf16 -> fp32 is exact).
+template <int OUT_DT>
+__global__ void embed_rows_vec_kernel(const int32_t* __restrict__ ids, const uint16_t* __restrict__ table,
+                                      void* __restrict__ out, int V, int H) {
+  const int t = blockIdx.x;
+  const int id = ids[t];
+  const bool ok = id >= 0 && id < V;
+  for (int i = 8 * threadIdx.x; i < H; i += 8 * blockDim.x) {
+    uint4 q = make_uint4(0, 0, 0, 0);
+    if (ok) q = *reinterpret_cast<const uint4*>(table + (int64_t)id * H + i);
+    if constexpr (OUT_DT == BIV_BF16) {
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + (int64_t)t * H + i) = q;
+    } else {
+      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+      float f[8];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        f[2 * c] = bf2f((uint16_t)(w[c] & 0xffffu));
+        f[2 * c + 1] = bf2f((uint16_t)(w[c] >> 16));
+      }
+      float* o = static_cast<float*>(out) + (int64_t)t * H + i;
+      *reinterpret_cast<f32x4*>(o) = f32x4{f[0], f[1], f[2], f[3]};
+      *reinterpret_cast<f32x4*>(o + 4) = f32x4{f[4], f[5], f[6], f[7]};
+    }
+  }
+}
+
 // One thread per (token, head, pair i < D/2).
 __global__ void rope_apply_kernel(void* __restrict__ x, int64_t stride, const int32_t* __restrict__ pos,
                                   const float* __restrict__ cos_sin, int T, int n_heads, int D, int max_pos,
@@ -219,6 +247,15 @@ extern "C" biv_status embed_rows(const int32_t* ids, const void* table, biv_dtyp
   BIV_REQUIRE(T >= 0 && V >= 1 && H >= 1, "embed_rows: bad sizes");
   if (T == 0) return BIV_OK;
   BIV_REQUIRE(ids && table && out, "embed_rows: NULL pointer");
+  if (table_dt == BIV_BF16 && H % 8 == 0 && aligned16(table) && aligned16(out)) {
+    if (out_dt == BIV_BF16)
+      hipLaunchKernelGGL(embed_rows_vec_kernel<BIV_BF16>, dim3(T), dim3(256), 0, static_cast<hipStream_t>(stream), ids,
+                         static_cast<const uint16_t*>(table), out, V, H);
+    else
+      hipLaunchKernelGGL(embed_rows_vec_kernel<BIV_F32>, dim3(T), dim3(256), 0, static_cast<hipStream_t>(stream), ids,
+                         static_cast<const uint16_t*>(table), out, V, H);
+    return launched("embed_rows");
+  }
   hipLaunchKernelGGL(embed_rows_kernel, dim3(T), dim3(256), 0, static_cast<hipStream_t>(stream), ids, table,
                      (int)table_dt, out, (int)out_dt, V, H);
   return launched("embed_rows");

@@ -818,3 +818,15 @@ def test_rope_swiglu_embed(biv, dtype):
     ref = np.zeros((6, 64))
     ref[:4] = oracle.as_f64(tab_np, dtype)[ids[:4]]
     assert np.array_equal(f64(emb), ref)
+    # output in the table's dtype, and a width that is not a multiple of 8
+    # (bf16: the 16-byte path above, the element loop here)
+    emb_t = torch.empty((6, 64), dtype=x.dtype, device=DEV)
+    biv.embed_rows(dev_i32(ids), dev(tab_np), emb_t)
+    tab2_np = mk(113, (50, 60))
+    emb2 = torch.empty((6, 60), dtype=torch.float32, device=DEV)
+    biv.embed_rows(dev_i32(ids), dev(tab2_np), emb2)
+    sync()
+    assert np.array_equal(f64(emb_t), ref)
+    ref2 = np.zeros((6, 60))
+    ref2[:4] = oracle.as_f64(tab2_np, dtype)[ids[:4]]
+    assert np.array_equal(f64(emb2), ref2)
