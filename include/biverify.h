@@ -87,7 +87,9 @@ biv_status rmsnorm_bi(const void* x, biv_dtype x_dt, const void* gamma, void* y,
 
 /* --------------------------------------------------------------------------
  * gemm_bi — batch-invariant matmul ([LLM42] para 1: no split-K; one and the
- * same data-parallel tiling for every batch size).
+ * same data-parallel tiling of the reduction for every batch size: each
+ * output is reduced by one workgroup in one fixed order, while the rows per
+ * output tile may shrink for small batches, which moves no bits).
  *
  *   acc[m, n] = sum_k A[m, k] * B[n, k]          (fp32 accumulation)
  *   epilogue BIV_EPI_STORE:  C[m, n] = acc

@@ -10,8 +10,9 @@
 // every output element is reduced by the 32x32x16 bf16 MFMA over
 // k = 0, 16, 32, ... in ascending order with fp32 accumulators, so its bits
 // depend only on its own row of A and column of B: not on M, not on the tile
-// it lands in, not on the other rows.  The tiling depends on the weight shape
-// alone and is the same for every M.
+// it lands in, not on the other rows.  This reduction is the same for every
+// M; the column tiling depends on the weight shape alone, and only the rows
+// per tile (32 or 64 at M <= 64, else the class's full height) follow M.
 //  - gemm_dma_kernel (K a multiple of 64, the decoder's case): A and B tiles
 //    copied HBM -> LDS by global_load_lds_dwordx4 into a ring of 64- or
 //    128-wide k stages; tile shape and wave arrangement chosen per weight width (see
@@ -501,8 +502,9 @@ static void launch_bf16(const void* A, const void* B, void* C, float* partial, i
                      tilesM, tilesN, k_per_split);
 }
 
-// Tile of the staged kernel for a weight with N outputs: one tiling per
-// weight shape, the same for every M.  (Each output's reduction order is the
+// Tile of the staged kernel for a weight with N outputs: one column tiling
+// per weight shape, the same for every M (rows per tile are cut for M <= 64,
+// below).  (Each output's reduction order is the
 // same under every tile -- one MFMA shape, ascending k -- so the tile only
 // decides which workgroup computes which outputs.)  Chosen by measurement:
 // at M = 512 on the decoder's weights, and for the 8192 <= N < 16384 class
