@@ -557,8 +557,8 @@ static void launch_dma_t(const void* A, const void* B, void* C, float* partial, 
 // No copies are spent on rows past M (a 128-row tile at M = 1 copies 128
 // activation rows per stage for one useful row), and the LDS this frees holds
 // a deeper ring of weight stages: small-M calls stream the weight, so the
-// weight bytes in flight per CU set their speed.  Rows, stages, waves along
-// M, for the tile classes above:
+// weight bytes in flight per CU set their speed.  Rows, columns, stages,
+// waves along M and along N, for the tile classes above:
 #define BIV_GEMM_L32_TILE 32, 256, 4, 1, 4   // 144 KiB, three weight stages in flight
 #define BIV_GEMM_L64_TILE 64, 256, 3, 2, 4   // 120 KiB
 #define BIV_GEMM_N32_TILE 32, 64, 8, 1, 2    // S and T classes: 96 KiB, seven stages in flight
