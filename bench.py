@@ -249,6 +249,114 @@ def gemm_only(args):
     print(json.dumps({"gemm_only": True, "M": W, "calls_per_matmul": args.iters + 3, "matmuls": out}), flush=True)
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+
+
+class KernelTimers:
+    """HIP event pairs around every call of the library's entry points during
+    eager passes, grouped by kernel class, on the stream the library launches
+    on (torch's current stream).  Installed by swapping the binding's module
+    functions (the pass looks them up at call time); removed afterwards."""
+
+    NAMES = ("embed_rows", "rmsnorm_bi", "gemm_bi", "rope_kv_overwrite", "attn_decode_bi",
+             "lm_head_gumbel_verify")
+
+    def __init__(self, torch):
+        import invariant_verify_verifier_amd._lib as L
+
+        self.torch, self.L = torch, L
+        self.pairs = {}
+        self.orig = {n: getattr(L, n) for n in self.NAMES}
+
+    @staticmethod
+    def key(name, args, kw):
+        if name == "gemm_bi":
+            a, b = args[0], args[1]
+            return ("gemm_bi", int(a.shape[0]), int(b.shape[0]), int(b.shape[1]), bool(kw.get("swiglu")),
+                    bool(kw.get("accumulate")), str(args[2].dtype).replace("torch.", ""))
+        return (name,)
+
+    def __enter__(self):
+        torch = self.torch
+        for n in self.NAMES:
+            fn = self.orig[n]
+
+            def run(*a, _n=n, _fn=fn, **k):
+                s = torch.cuda.Event(enable_timing=True)
+                e = torch.cuda.Event(enable_timing=True)
+                s.record()
+                r = _fn(*a, **k)
+                e.record()
+                self.pairs.setdefault(self.key(_n, a, k), []).append((s, e))
+                return r
+
+            setattr(self.L, n, run)
+        return self
+
+    def __exit__(self, *exc):
+        for n, fn in self.orig.items():
+            setattr(self.L, n, fn)
+
+    def mean_ms(self):
+        self.torch.cuda.synchronize()
+        return {k: (float(np.mean([s.elapsed_time(e) for s, e in v])), len(v)) for k, v in self.pairs.items()}
+
+
+def kernel_rooflines(sh, W, ctx, timers, steps):
+    """Per kernel class of the pass: algorithmic bytes and FLOPs per call, the
+    bound (HBM or bf16 MFMA, whichever takes longer at the published peaks),
+    the mean HIP-event time per call, and achieved / peak.  Also the whole
+    step's roofline time: the sum over every call of its roofline time."""
+    H, D, F, V = sh.hidden, sh.head_dim, sh.ffn, sh.vocab
+    kv_tok = sh.kv_heads * D * 2  # bf16 bytes of one token's K (or V) in one layer
+    out, t_roof_step = {}, 0.0
+    for key, (ms, n) in sorted(timers.items(), key=lambda kv: -kv[1][0] * kv[1][1]):
+        name = key[0]
+        flop = 0.0
+        if name == "gemm_bi":
+            _, M, N, K, swiglu, acc, odt = key
+            ob = 2 if odt == "bfloat16" else 4
+            n_out = N // 2 if swiglu else N
+            flop = 2.0 * M * N * K
+            nbytes = N * K * 2 + M * K * 2 + M * n_out * ob * (2 if acc else 1)
+            label = {(6144, 4096): "gemm_bi QKV", (4096, 4096): "gemm_bi O + residual",
+                     (28672, 4096): "gemm_bi gate|up + SwiGLU", (4096, 14336): "gemm_bi down + residual"}.get(
+                         (N, K), f"gemm_bi N={N} K={K}")
+        elif name == "attn_decode_bi":
+            nbytes = float(np.sum(ctx.astype(np.int64) + K_CAND)) * kv_tok * 2
+            flop = 4.0 * float(np.sum(ctx.astype(np.int64) + K_CAND)) * K_CAND * sh.heads * D  # QK and PV
+            label = "attn_decode_bi"
+        elif name == "rmsnorm_bi":
+            nbytes = W * H * (4 + 2) + H * 2
+            label = "rmsnorm_bi (fp32 stream -> bf16)"
+        elif name == "rope_kv_overwrite":
+            nbytes = W * (sh.heads + sh.kv_heads) * D * 2 * 2 + W * sh.kv_heads * D * 2 + W * kv_tok * 2
+            label = "rope_kv_overwrite"
+        elif name == "embed_rows":
+            nbytes = W * H * (2 + 4)
+            label = "embed_rows"
+        elif name == "lm_head_gumbel_verify":
+            flop = 2.0 * W * H * V
+            nbytes = V * H * 2 + W * V * 4 + W * H * 2
+            label = "lm_head_gumbel_verify (lm_head matmul + Gumbel argmax + verify)"
+        else:
+            continue
+        t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+        t_mfma = flop / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+        t_roof = max(t_hbm, t_mfma)
+        per_step = n / steps
+        t_roof_step += t_roof * per_step
+        if t_mfma > t_hbm:
+            ach, peak, unit, bound = flop / (ms / 1e3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
+        else:
+            ach, peak, unit, bound = nbytes / (ms / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
+        out[label] = {"bound": bound, "achieved": round(ach, 1), "peak": peak, "unit": unit,
+                      "frac": round(ach / peak, 4), "calls_per_step": per_step, "avg_launch_ms": round(ms, 5),
+                      "bytes_per_launch": nbytes, "flop_per_launch": flop,
+                      "share_of_step_ms": round(ms * per_step, 4)}
+    return out, t_roof_step * 1e3
+
+
 class EventTimer:
     """HIP event pairs around every launch of one kernel, on its stream."""
 
@@ -361,6 +469,12 @@ def gpu_state_under_load(torch, replay, limit_s=20):
             "cards": keep}
 
 
+def _dvr_event_ms(fn, iters=5, warmup=2):
+    from invariant_verify_verifier_amd.dvr import _event_ms
+
+    return _event_ms(fn, iters=iters, warmup=warmup)
+
+
 def time_passes(torch, model, batch, caches, steps, **kw):
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -372,14 +486,43 @@ def time_passes(torch, model, batch, caches, steps, **kw):
     return start.elapsed_time(end) / steps
 
 
+def _host_cpu():
+    """The host's CPU model (lscpu's "Model name", else /proc/cpuinfo), the
+    cores this process may run on, and the logical CPUs the host reports."""
+    import platform
+    import subprocess
+
+    model = None
+    try:
+        p = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10)
+        for ln in p.stdout.splitlines():
+            if ln.strip().lower().startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except (OSError, subprocess.SubprocessError):
+        pass
+    if model is None:
+        try:
+            with open("/proc/cpuinfo") as f:
+                for ln in f:
+                    if ln.lower().startswith("model name"):
+                        model = ln.split(":", 1)[1].strip()
+                        break
+        except OSError:
+            model = platform.processor() or None
+    return {"model": model, "affinity_cores": len(os.sched_getaffinity(0)), "nproc": os.cpu_count()}
+
+
 def cpu_baseline(torch, env, n_layers, sample_layers=3):
     """The oracle, untouched, on a bounded sample of the same workload: the
     first `sample_layers` decoder layers over all 512 rows, then the final
     norm, lm_head and verify; extrapolated to the full depth as
-    n_layers * mean(t_layer) + t_head per pass."""
+    n_layers * mean(t_layer) + t_head per pass.  Run with NumPy's BLAS on
+    every core this process may use, then once more on one thread for one
+    layer of the sample (the rate per row is the same work per row)."""
     import oracle
     import workloads as wl
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     sh, dw, lay, ctx = env["sh"], env["dw"], env["lay"], env["ctx"]
     n = N_REQ
@@ -390,12 +533,17 @@ def cpu_baseline(torch, env, n_layers, sample_layers=3):
         b = t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
         return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
+    host = _host_cpu()
+    cores = host["affinity_cores"]
+    limiter = threadpool_limits(limits=cores)
+    blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     used = sorted({int(b) for b in lay.block_table[:n].ravel() if b >= 0})
     remap = {b: i for i, b in enumerate(used)}
     bt = np.vectorize(lambda b: remap.get(int(b), -1))(lay.block_table[:n]).astype(np.int32)
     toks = np.concatenate([env["t0"][:n, None], env["cand"][:n, :K_CAND - 1]], axis=1)
     lm = f64(dw["lm_head"])
     t_layers = []
+    one_thread = None
     for li in range(min(sample_layers, n_layers)):
         Ld = dw["layers"][li]
         wqkv, wgu = f64(Ld["wqkv"]), f64(Ld["w_gu"])
@@ -411,6 +559,21 @@ def cpu_baseline(torch, env, n_layers, sample_layers=3):
         t = time.perf_counter()
         oracle.decoder_forward(ow, toks, ctx[:n], [kc], [vc], bt)
         t_layers.append(time.perf_counter() - t)
+        if li == 0:
+            # the same layer on one thread, over the first 8 requests (64 rows)
+            n1 = 8
+            used1 = sorted({int(b) for b in lay.block_table[:n1].ravel() if b >= 0})
+            kc1 = f64(env["caches"][li][0][used1])
+            vc1 = f64(env["caches"][li][1][used1])
+            remap1 = {b: i for i, b in enumerate(used1)}
+            bt1 = np.vectorize(lambda b: remap1.get(int(b), -1))(lay.block_table[:n1]).astype(np.int32)
+            with threadpool_limits(limits=1):
+                t = time.perf_counter()
+                oracle.decoder_forward(ow, toks[:n1], ctx[:n1], [kc1], [vc1], bt1)
+                t1 = time.perf_counter() - t
+            one_thread = {"rows": n1 * K_CAND, "t_layer_s": round(t1, 3),
+                          "rows_per_s_per_layer": round(n1 * K_CAND / t1, 3)}
+            del kc1, vc1
         del kc, vc, wqkv, wgu, layer
     x = wl.normal_f32(1, (n * K_CAND, H)).astype(np.float64)
     t = time.perf_counter()
@@ -419,12 +582,21 @@ def cpu_baseline(torch, env, n_layers, sample_layers=3):
     t_head = time.perf_counter() - t
     t_layer = float(np.mean(t_layers))
     t_pass = n_layers * t_layer + t_head
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": round(n * K_CAND / t_pass, 3), "unit": "verified tok/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{len(t_layers)} of {n_layers} layers + lm_head/verify over all {n * K_CAND} rows, fp64; "
-                      f"t_layer={t_layer:.2f}s (mean) t_head={t_head:.2f}s; pass = {n_layers}*t_layer + t_head "
-                      f"(extrapolated)"}
+    limiter.restore_original_limits()
+    out = {"value": round(n * K_CAND / t_pass, 3), "unit": "verified tok/s", "cores": int(cores),
+           "kind": "oracle",
+           "sample": f"{len(t_layers)} of {n_layers} layers + lm_head/verify over all {n * K_CAND} rows, fp64; "
+                     f"t_layer={t_layer:.2f}s (mean) t_head={t_head:.2f}s; pass = {n_layers}*t_layer + t_head "
+                     f"(extrapolated); matmuls on NumPy's BLAS with {blas_threads} threads, the attention's "
+                     f"per-row loop in one Python thread",
+           "host_cpu": host, "blas_threads": int(blas_threads)}
+    if one_thread is not None:
+        one_thread["pass_extrapolated_tok_s"] = round(
+            one_thread["rows_per_s_per_layer"] / n_layers, 4)
+        one_thread["note"] = ("layer 0 over the first 8 requests on one thread; pass = rows / (32 * t_layer), "
+                              "head not included")
+        out["single_thread"] = one_thread
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -859,6 +1031,11 @@ def main():
     timer.on = True
     ms_eager = time_passes(torch, model, batch, caches, args.steps, attn_fn=attn, fused_head=True)
     timer.on = False
+    # eager passes with HIP events around every call of every kernel class
+    # (per-kernel rooflines and the whole step's)
+    with KernelTimers(torch) as kt:
+        time_passes(torch, model, batch, caches, args.steps, fused_head=True)
+    per_kernel, roof_ms_step = kernel_rooflines(env["sh"], N_REQ * K_CAND, ctx, kt.mean_ms(), args.steps)
     # the timed step: the whole pass replayed as one HIP graph
     graph = model.capture(batch, caches, fused_head=True)
     for _ in range(args.warmup):
@@ -886,9 +1063,30 @@ def main():
     print("[bench] split-K / adaptive-split variant pass", file=sys.stderr, flush=True)
     from invariant_verify_verifier_amd.dvr import SplitKernels
 
-    var = SplitKernels(N_REQ, env["sh"].kv_heads, env["lay"].max_blocks)
-    model.verify(batch, caches, attn_fn=var.attn, gemm_fn=var.gemm, fused_head=True)
+    var = SplitKernels(N_REQ, env["sh"].kv_heads, env["lay"].max_blocks, tune=True)
+    model.verify(batch, caches, attn_fn=var.attn, gemm_fn=var.gemm, fused_head=True)  # tunes each shape once
     torch.cuda.synchronize()
+    # the invariant attention call, timed the way the variant's candidates were
+    sh_ = env["sh"]
+    a_q = torch.empty((N_REQ * K_CAND, sh_.heads * sh_.head_dim), dtype=torch.bfloat16, device="cuda").normal_()
+    a_o = torch.empty((N_REQ * K_CAND, sh_.heads, sh_.head_dim), dtype=torch.bfloat16, device="cuda")
+    t_attn_bi = _dvr_event_ms(lambda: biv.attn_decode_bi(a_q, caches[0][0], caches[0][1], batch.block_table, batch.ctx,
+                                                         a_o, K_CAND, 1.0 / math.sqrt(sh_.head_dim),
+                                                         model.workspace(N_REQ, env["lay"].max_blocks, K_CAND)))
+    per_shape = {}
+    for key, t in var.timings.items():
+        if key[0] == "gemm":
+            _, M_, N_, K_ = key
+            best = var.splits[(M_, N_, K_)]
+            per_shape[f"gemm M={M_} N={N_} K={K_}"] = {
+                "us_by_splits": t, "chosen_splits": best,
+                "t_invariant_us": t[1], "t_variant_us": t[best], "slowdown": round(t[1] / t[best], 4)}
+        else:
+            best = var.attn_splits[key[1:]]
+            per_shape[f"attention R={key[1]} q_len={key[2]}"] = {
+                "us_by_split_tokens": t, "chosen_split_tokens": best,
+                "t_invariant_us": round(t_attn_bi * 1e3, 2), "t_variant_us": t[best],
+                "slowdown": round(t_attn_bi * 1e3 / t[best], 4)}
     ms_var = time_graph(torch, model, batch, caches, args.steps, args.warmup, attn_fn=var.attn, gemm_fn=var.gemm,
                         fused_head=True)
     tgt_var = batch.target.cpu().numpy()
@@ -919,10 +1117,11 @@ def main():
                    "launch": "whole pass captured as one HIP graph; lm_head + Gumbel verify fused",
                    "wall_s_timed": round(wall, 3)},
         "slowdown_vs_splitk": {"value": round(ms_step / ms_var, 4), "ms_variant": round(ms_var, 4),
-                               "variant": "gemm_splitk (auto splits per shape: "
-                                          + ", ".join(f"N={n},K={k}:{sp}" for (n, k), sp in sorted(var.splits.items()))
-                                          + f") + attn_decode_adaptive (split {var.split} tokens); "
-                                          "same fused lm_head + Gumbel verify",
+                               "variant": "gemm_splitk and attn_decode_adaptive with the split of each shape "
+                                          "chosen by timing the candidates (GEMM splits 1/2/4/8, 1 = the "
+                                          "invariant kernel; KV splits 256*2^k tokens); same fused lm_head + "
+                                          "Gumbel verify",
+                               "per_shape": per_shape,
                                "target_rows_differing": int((tgt_var != tgt_bi).sum()),
                                "accept_len_differing": int((acc_var != acc_bi).sum())},
         "roofline": {"kernel": "attn_decode_bi (attn_bf16_kernel + attn_combine_kernel)", "bound": "hbm",
@@ -930,6 +1129,11 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
                      "bytes_per_launch": attn_bytes, "avg_launch_ms": round(attn_ms, 5),
                      "launches_timed": len(timer.pairs)},
+        "roofline_per_kernel": per_kernel,
+        "roofline_step": {"roofline_ms": round(roof_ms_step, 4), "ms_per_step": round(ms_step, 4),
+                          "frac": round(roof_ms_step / ms_step, 4),
+                          "note": "sum over every call of the pass of max(algorithmic bytes / 8 TB/s, "
+                                  "FLOP / 2.5 PFLOP/s bf16) at this run's contexts, divided by the timed step"},
         "cpu_baseline": None,
         "gpu_state": gpu_state,
     }

@@ -72,17 +72,30 @@ const char* biv_last_error(void);
 /* --------------------------------------------------------------------------
  * rmsnorm_bi — batch-invariant RMSNorm ([LLM42] para 1: RMSNorm with a fixed
  * split over the hidden dimension, independent of how many compute units are
- * busy).
+ * busy), with an optional residual add in the same pass.
  *
- *   y[m, i] = x[m, i] * gamma[i] / sqrt(mean_k x[m, k]^2 + eps)
+ *   residual == NULL:  s[m, i] = x[m, i]
+ *   residual != NULL:  s[m, i] = fl32(x[m, i] + residual[m, i]), rounded once
+ *                      to x_dt and written back to residual[m, i]
+ *   y[m, i] = s[m, i] * gamma[i] / sqrt(mean_k s[m, k]^2 + eps)
  *
- * x [M, H] in x_dt; gamma [H] and y [M, H] in y_dt (device).  The sum of
- * squares of a row is accumulated in fp32 in an order fixed by H alone: lane
- * t of a 256-lane workgroup adds elements t, t+256, ... in ascending order,
- * then a fixed butterfly over lanes and a fixed ascending sum over waves.
- * M >= 0 (M = 0 launches nothing), 1 <= H <= 65536.  x and y may not overlap.
+ * x [M, H] and residual [M, H] (nullable) in x_dt; gamma [H] and y [M, H] in
+ * y_dt (device).  The sum of squares of a row is accumulated in fp32 with
+ * fused multiply-adds in an order fixed by H alone, never by M, the
+ * pointers' alignment or the other rows: one 256-lane workgroup per row;
+ * when H is a multiple of 1024, lane t adds the 4-element groups
+ * 4t + 1024j (j ascending, the four elements in ascending order), otherwise
+ * elements t, t+256, ... in ascending order; then a fixed butterfly over
+ * the 64 lanes of each wave and the four wave sums added in ascending order.
+ * M >= 0 (M = 0 launches nothing), 1 <= H <= 65536.  x, residual and y may
+ * not overlap (BIV_EINVAL).
+ *
+ * The decoder forward here keeps its residual stream in fp32 and adds each
+ * sublayer's output inside the matmul that produces it (gemm_bi's
+ * BIV_EPI_ACCUM), so it calls rmsnorm_bi with residual == NULL; the fused
+ * form serves callers whose sublayer outputs are separate tensors.
  * ------------------------------------------------------------------------ */
-biv_status rmsnorm_bi(const void* x, biv_dtype x_dt, const void* gamma, void* y, biv_dtype y_dt,
+biv_status rmsnorm_bi(const void* x, biv_dtype x_dt, void* residual, const void* gamma, void* y, biv_dtype y_dt,
                       int64_t M, int64_t H, float eps, biv_stream stream);
 
 /* --------------------------------------------------------------------------
@@ -120,19 +133,33 @@ biv_status gemm_bi(const void* A, const void* B, void* C, int64_t M, int64_t N, 
  * para 1: a fixed KV-split size, no adaptation to sequence length or load;
  * para 3-4: the verifier runs K query rows per request).
  *
- * Row (r, j), j < q_len, is the query of the token at absolute position
+ * Row (r, j), j < q_len_r, is the query of the token at absolute position
  * ctx[r] + j; it attends to keys at positions 0 .. ctx[r] + j of request r:
  *   out = softmax(q . k_p * scale) . v_p,  q head h reads KV head h / (Hq/Hkv).
  *
- * q   R*q_len rows of Hq*D elements (row r*q_len + j), consecutive rows
- *     q_stride elements apart (>= Hq*D; a slice of a fused QKV output
- *     can be passed directly)                      dt, device
+ * Rows of a request (the K candidates of each of N requests, [LLM42] para 4;
+ * requests may bring different numbers of candidates):
+ *   q_off == NULL: every request has q_len rows; row (r, j) is row
+ *                  r*q_len + j of q and out.
+ *   q_off != NULL: device int32 [R+1], non-decreasing, q_off[0] = 0; request
+ *                  r has q_len_r = q_off[r+1] - q_off[r] rows (0 <= q_len_r
+ *                  <= q_len; q_len is then the largest q_len_r, which sizes
+ *                  the grid and the workspace), row (r, j) is row
+ *                  q_off[r] + j of q and out, and q and out hold q_off[R]
+ *                  rows.  The offsets are read on the device; rows past
+ *                  q_len of a request are not computed.  A row's bits are the
+ *                  same as with q_off == NULL and that request alone: they do
+ *                  not depend on the other requests' row counts.
+ *
+ * q   the rows above, Hq*D elements each, consecutive rows q_stride
+ *     elements apart (>= Hq*D; a slice of a fused QKV output can be passed
+ *     directly)                                    dt, device
  * k_cache, v_cache [num_blocks, Hkv, 16, D]        dt, device (pages of 16)
  * block_table [R, max_blocks] int32: physical page of each logical page;
  *             entries outside [0, num_blocks) are treated as empty pages
  *             (their keys are masked, their values read as zero).
  * ctx [R] int32: verified context length L_r >= 0 of each request.
- * out [R*q_len, Hq, D]                             dt, device
+ * out [rows, Hq, D]                                dt, device
  *
  * Keys are cut into 256-token chunks aligned at absolute position 0.  Each
  * chunk gives a partial (max, sum, weighted values) for each row; partials
@@ -140,11 +167,11 @@ biv_status gemm_bi(const void* A, const void* B, void* C, int64_t M, int64_t N, 
  * BIV_ATTN_SEG_TOKENS tokens, and the segment results are left-folded in
  * ascending order.  Every split point is a fixed absolute position, so a
  * row's result depends only on its own request's data and length.
- * Positions >= ctx[r] + q_len read as empty (values zero, keys masked).
+ * Positions >= ctx[r] + q_len_r read as empty (values zero, keys masked).
  * Two launches: the chunk/segment pass, then (only when some request spans
  * more than one segment, or segments are split) the fold of the partials;
  * large grids add a one-workgroup launch before them that orders the
- * segments.  Where the grid of segments would hold fewer than 1024 waves
+ * segments.  Where the grid of segments would hold fewer than 512 waves
  * (decided by R, Hkv and max_blocks alone), each segment is taken by
  * several waves over consecutive 256-token chunks: the first folds its
  * chunks, the later ones store their chunk partials, and the second launch
@@ -157,7 +184,7 @@ biv_status gemm_bi(const void* A, const void* B, void* C, int64_t M, int64_t N, 
  * time, each such row block with its own keys 0 .. ctx[r] + its last
  * position, so q_len up to a whole prompt gives a causal prefill whose rows
  * are the same bits as decoding them one at a time); dt BIV_F32 with D in
- * {64, 128} (fp32 path, any q_len).  Hq % Hkv == 0, ctx[r] + q_len <=
+ * {64, 128} (fp32 path, any q_len).  Hq % Hkv == 0, ctx[r] + q_len_r <=
  * max_blocks * 16, R * row blocks <= 65535.
  *
  * workspace: device memory of at least
@@ -179,8 +206,8 @@ size_t biv_attn_workspace_bytes(int R, int Hkv, int max_blocks, int seg_tokens);
 size_t biv_attn_workspace_bytes_q(int R, int q_len, int Hq, int Hkv, int max_blocks, int seg_tokens);
 
 biv_status attn_decode_bi(const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
-                          const int32_t* block_table, const int32_t* ctx, void* out, int R, int q_len,
-                          int Hq, int Hkv, int D, int max_blocks, int num_blocks, float scale,
+                          const int32_t* block_table, const int32_t* ctx, const int32_t* q_off, void* out, int R,
+                          int q_len, int Hq, int Hkv, int D, int max_blocks, int num_blocks, float scale,
                           biv_dtype dt, void* workspace, size_t workspace_bytes, biv_stream stream);
 
 /* --------------------------------------------------------------------------
@@ -339,9 +366,17 @@ biv_status swiglu(const void* gu, void* out, int64_t M, int64_t N, int64_t block
  * para 1: split-K matmul; attention whose split adapts to length and load).
  * ------------------------------------------------------------------------ */
 
-/* gemm_splitk: bf16 A/B as in gemm_bi, fp32 partial sums of `splits` slices
- * of K reduced in a second pass.  splits == 0 picks the count from M, N, K so
- * that the grid fills the GPU.  workspace: biv_splitk_workspace_bytes(). */
+/* gemm_splitk: bf16 A/B as in gemm_bi (epilogues STORE, ACCUM and SWIGLU),
+ * fp32 partial sums of `splits` slices of K (each a multiple of 64 wide)
+ * computed by the staged kernel on its own tiles and summed in ascending
+ * slice order by a second pass that applies the epilogue.  A split count of 1
+ * is gemm_bi itself (no partials, no second pass).  splits == 0 picks the
+ * count from M, N, K: doubled from 1 while the staged kernel's grid holds
+ * fewer workgroups than the GPU has compute units, up to 8, keeping at least
+ * four k stages per slice.  Which count is fastest depends on the shape; a
+ * caller tuning for speed times the candidates (the results differ in the
+ * last bits between counts and between M, which is the point of the
+ * comparison).  workspace: biv_splitk_workspace_bytes() (unused at 1). */
 size_t biv_splitk_workspace_bytes(int64_t M, int64_t N, int splits);
 /* The split count gemm_splitk uses for splits == 0. */
 int biv_splitk_auto_splits(int64_t M, int64_t N, int64_t K);

@@ -24,7 +24,11 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     # packed fp32 instructions off for all device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-ffp-contract=fast",
+    # no implicit contraction of a*b + c: every fused multiply-add in the
+    # kernels is written out (fmaf / __fmaf_rn), so two kernels that state
+    # the same arithmetic round it the same way whatever the compiler
+    # schedules (several bit-for-bit equalities between kernels rest on it)
+    "-ffp-contract=off",
 ]
 # Per-source extras.  The attention kernel runs one wave per SIMD and also
 # rescales and folds its MFMA accumulators with vector ALU code: keeping MFMA

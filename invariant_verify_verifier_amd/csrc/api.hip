@@ -16,7 +16,7 @@ void set_error(const char* fmt, ...) {
 
 }  // namespace biv
 
-extern "C" int biv_abi_version(void) { return 1; }
+extern "C" int biv_abi_version(void) { return 2; }
 
 extern "C" const char* biv_last_error(void) { return biv::g_last_error; }
 

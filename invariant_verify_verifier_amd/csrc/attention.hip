@@ -66,6 +66,18 @@ __device__ __forceinline__ int pick_window(int w, int w0, int w1, int w2, int w3
   return w == 0 ? w0 : (w == 1 ? w1 : (w == 2 ? w2 : (w == 3 ? w3 : wx)));
 }
 
+// Rows of request r: q_len_r = q_off[r+1] - q_off[r] (clamped to [0, q_len])
+// starting at row q_off[r], or q_len rows from row r*q_len without q_off.
+struct ReqRows {
+  int64_t first;  // row of position ctx[r] + 0
+  int n;          // rows (0: the request has none)
+};
+__device__ __forceinline__ ReqRows req_rows(const int32_t* __restrict__ q_off, int r, int q_len) {
+  if (q_off == nullptr) return {(int64_t)r * q_len, q_len};
+  const int a = q_off[r], b = q_off[r + 1];
+  return {(int64_t)a, a < 0 ? 0 : min(max(b - a, 0), q_len)};
+}
+
 struct AttnWs {
   float* part_o;   // [slot][16 groups][64 lanes][4]: values 4q .. 4q+3 of a lane in group q
   float* part_ml;  // [slot][64 lanes][2]
@@ -134,7 +146,8 @@ template <bool kParts>
 __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx,
-    uint16_t* __restrict__ out, int q_len, int Hq, int Hkv, int max_blocks, int num_blocks, float scale_log2,
+    const int32_t* __restrict__ q_off, uint16_t* __restrict__ out, int q_len, int Hq, int Hkv, int max_blocks,
+    int num_blocks, float scale_log2,
     int seg_tokens, int nseg_max, AttnWs ws, const int32_t* __restrict__ items, int blk_pos, int n_rb, int parts,
     int head_fastest) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kRing * kSlot];
@@ -174,7 +187,9 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
   const int tok_begin = seg * seg_tokens + part * part_tok;  // a multiple of kChunk
   const int r = v / n_rb, j0 = (v - r * n_rb) * blk_pos;  // request, first query position of the block
   const int lane = threadIdx.x, g = lane >> 5, li = lane & 31;
-  const int G = Hq / Hkv, jn = min(blk_pos, q_len - j0), nrows = jn * G;
+  const ReqRows rr = req_rows(q_off, r, q_len);
+  const int G = Hq / Hkv, jn = min(blk_pos, rr.n - j0), nrows = jn * G;
+  if (jn <= 0) return;  // a row block past the request's rows
   const int32_t* bt = block_table + (int64_t)r * max_blocks;
   const int page0 = tok_begin >> 4;  // first page of the part
 
@@ -192,7 +207,7 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
   const bool row_ok = li < nrows;
   const int jq = j0 + (row_ok ? li / G : 0);
   const int hq = kvh * G + (row_ok ? li % G : 0);
-  const int64_t qtok = (int64_t)r * q_len + jq;
+  const int64_t qtok = rr.first + jq;
   bf16x8 bq[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
@@ -472,7 +487,8 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
 // the work changes: each item's arithmetic and its workspace slot are fixed
 // by (request, segment), so the results are the same bits.  One workgroup;
 // partial lengths are bucketed in 128 classes.
-__global__ __launch_bounds__(1024) void attn_plan_kernel(const int32_t* __restrict__ ctx, int Rv, int q_len,
+__global__ __launch_bounds__(1024) void attn_plan_kernel(const int32_t* __restrict__ ctx,
+                                                        const int32_t* __restrict__ q_off, int Rv, int q_len,
                                                         int max_blocks, int seg_tokens, int nseg_max, int blk_pos,
                                                         int n_rb, int32_t* __restrict__ items) {
   constexpr int NB = 128;
@@ -489,10 +505,12 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(const int32_t* __restri
   __syncthreads();
   const int cap = max_blocks * 16;
   const int bw = (seg_tokens + NB - 1) / NB;
-  // keys of row block v: up to the block's last query position
+  // keys of row block v: up to the block's last query position (none for a
+  // block past its request's rows)
   auto block_tokens = [&](int v) {
     const int r = v / n_rb, j0 = (v - r * n_rb) * blk_pos;
-    return min(ctx[r] + j0 + min(blk_pos, q_len - j0), cap);
+    const int jn = min(blk_pos, req_rows(q_off, r, q_len).n - j0);
+    return jn <= 0 ? 0 : min(ctx[r] + j0 + jn, cap);
   };
   for (int v = tid; v < Rv; v += 1024) {
     const int nt = block_tokens(v);
@@ -588,6 +606,7 @@ constexpr int kCombZ = 4;  // workgroups per (KV head, row block)
 constexpr int kCombThreads = 1024 / kCombZ, kCombBatch = 8, kChunkBatch = 4;
 
 __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(const int32_t* __restrict__ ctx,
+                                                                    const int32_t* __restrict__ q_off,
                                                                     uint16_t* __restrict__ out, int q_len, int Hq,
                                                                     int Hkv, int max_blocks, int seg_tokens,
                                                                     int nseg_max, AttnWs ws, int blk_pos, int n_rb,
@@ -596,7 +615,9 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(const int32_
   const int r = v / n_rb, j0 = (v - r * n_rb) * blk_pos;
   const int tid = threadIdx.x, q = blockIdx.z * (kCombThreads / 64) + (tid >> 6), lane = tid & 63, g = lane >> 5,
             li = lane & 31;
-  const int G = Hq / Hkv, jn = min(blk_pos, q_len - j0), nrows = jn * G;
+  const ReqRows rr = req_rows(q_off, r, q_len);
+  const int G = Hq / Hkv, jn = min(blk_pos, rr.n - j0), nrows = jn * G;
+  if (jn <= 0) return;
   const int n_tok = min(ctx[r] + j0 + jn, max_blocks * 16);
   const int nseg = (n_tok + seg_tokens - 1) / seg_tokens;
   const int part_tok = seg_tokens / parts, cps = seg_tokens / kChunk, cpp = part_tok / kChunk;
@@ -655,7 +676,7 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(const int32_
     }
   }
   const float inv = Lt > 0.0f ? __fdiv_rn(1.0f, Lt) : 0.0f;
-  uint16_t* orow = out + (((int64_t)r * q_len + jq) * Hq + hq) * kHD + 32 * (q >> 2) + 8 * (q & 3) + 4 * g;
+  uint16_t* orow = out + ((rr.first + jq) * Hq + hq) * kHD + 32 * (q >> 2) + 8 * (q & 3) + 4 * g;
   const uint32_t w0 = (uint32_t)f2bf(__fmul_rn(O[0], inv)) | ((uint32_t)f2bf(__fmul_rn(O[1], inv)) << 16);
   const uint32_t w1 = (uint32_t)f2bf(__fmul_rn(O[2], inv)) | ((uint32_t)f2bf(__fmul_rn(O[3], inv)) << 16);
   *reinterpret_cast<uint2*>(orow) = make_uint2(w0, w1);
@@ -669,18 +690,21 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
                                                       const float* __restrict__ k_cache,
                                                       const float* __restrict__ v_cache,
                                                       const int32_t* __restrict__ block_table,
-                                                      const int32_t* __restrict__ ctx, float* __restrict__ out,
+                                                      const int32_t* __restrict__ ctx,
+                                                      const int32_t* __restrict__ q_off, float* __restrict__ out,
                                                       int q_len, int Hq, int Hkv, int D, int max_blocks,
                                                       int num_blocks, float scale) {
   __shared__ float qs[128];
   __shared__ float ps[kChunk];
   const int j = blockIdx.x, h = blockIdx.y, r = blockIdx.z;
   const int lane = threadIdx.x;
+  const ReqRows rr = req_rows(q_off, r, q_len);
+  if (j >= rr.n) return;
   const int G = Hq / Hkv, kvh = h / G;
   const int L = ctx[r];
   const int n_keys = min(L + j + 1, max_blocks * 16);
   const int32_t* bt = block_table + (int64_t)r * max_blocks;
-  const int64_t qtok = (int64_t)r * q_len + j;
+  const int64_t qtok = rr.first + j;
   const int64_t qrow = qtok * Hq + h;
   for (int d = lane; d < D; d += 64) qs[d] = q[qtok * q_stride + (int64_t)h * D + d];
   __syncthreads();
@@ -760,7 +784,8 @@ static inline int attn_blk_pos(int Hq, int Hkv) { return 32 / (Hq / Hkv); }
 static inline int attn_row_blocks(int q_len, int Hq, int Hkv) { return (int)cdiv(q_len, attn_blk_pos(Hq, Hkv)); }
 
 static biv_status launch_attn_bf16(const char* who, const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
-                                   const int32_t* block_table, const int32_t* ctx, void* out, int R, int q_len,
+                                   const int32_t* block_table, const int32_t* ctx, const int32_t* q_off, void* out,
+                                   int R, int q_len,
                                    int Hq, int Hkv, int max_blocks, int num_blocks, float scale, int seg_tokens,
                                    bool allow_split, void* workspace, size_t workspace_bytes, hipStream_t s) {
   const int G = Hq / Hkv;
@@ -787,7 +812,7 @@ static biv_status launch_attn_bf16(const char* who, const void* q, int64_t q_str
   dim3 grid((unsigned)(nseg_max * parts), Hkv, Rv);
   if (parts == 1 && waves >= 4 * (int64_t)resident_attn_waves() && waves <= 0x7fffffff) {
     items = attn_ws_items(workspace, Rv, Hkv, nseg_max);
-    hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, s, ctx, Rv, q_len, max_blocks, seg_tokens, nseg_max,
+    hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, s, ctx, q_off, Rv, q_len, max_blocks, seg_tokens, nseg_max,
                        blk_pos, n_rb, items);
     biv_status st = launched(who);
     if (st != BIV_OK) return st;
@@ -805,16 +830,16 @@ static biv_status launch_attn_bf16(const char* who, const void* q, int64_t q_str
   if (parts > 1)
     hipLaunchKernelGGL(attn_bf16_kernel<true>, grid, dim3(64), 0, s, static_cast<const uint16_t*>(q), q_stride,
                        static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache), block_table, ctx,
-                       static_cast<uint16_t*>(out), q_len, Hq, Hkv, max_blocks, num_blocks, scale * kLog2e,
+                       q_off, static_cast<uint16_t*>(out), q_len, Hq, Hkv, max_blocks, num_blocks, scale * kLog2e,
                        seg_tokens, nseg_max, ws, items, blk_pos, n_rb, parts, 0);
   else
     hipLaunchKernelGGL(attn_bf16_kernel<false>, grid, dim3(64), 0, s, static_cast<const uint16_t*>(q), q_stride,
                        static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache), block_table, ctx,
-                       static_cast<uint16_t*>(out), q_len, Hq, Hkv, max_blocks, num_blocks, scale * kLog2e,
+                       q_off, static_cast<uint16_t*>(out), q_len, Hq, Hkv, max_blocks, num_blocks, scale * kLog2e,
                        seg_tokens, nseg_max, ws, items, blk_pos, n_rb, 1, head_fastest ? 1 : 0);
   biv_status st = launched(who);
   if (st != BIV_OK || (nseg_max <= 1 && parts == 1)) return st;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(Hkv, Rv, kCombZ), dim3(kCombThreads), 0, s, ctx, static_cast<uint16_t*>(out),
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(Hkv, Rv, kCombZ), dim3(kCombThreads), 0, s, ctx, q_off, static_cast<uint16_t*>(out),
                      q_len, Hq, Hkv, max_blocks, seg_tokens, nseg_max, ws, blk_pos, n_rb, parts);
   return launched(who);
 }
@@ -837,7 +862,8 @@ extern "C" size_t biv_attn_workspace_bytes_q(int R, int q_len, int Hq, int Hkv, 
 }
 
 extern "C" biv_status attn_decode_bi(const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
-                                     const int32_t* block_table, const int32_t* ctx, void* out, int R, int q_len,
+                                     const int32_t* block_table, const int32_t* ctx, const int32_t* q_off, void* out,
+                                     int R, int q_len,
                                      int Hq, int Hkv, int D, int max_blocks, int num_blocks, float scale,
                                      biv_dtype dt, void* workspace, size_t workspace_bytes, biv_stream stream) {
   using namespace biv;
@@ -851,12 +877,12 @@ extern "C" biv_status attn_decode_bi(const void* q, int64_t q_stride, const void
     if (D != kHD) return fail(BIV_EUNSUPPORTED, "attn_decode_bi: bf16 path supports D == 128 only (D=%d)", D);
     if (32 % (Hq / Hkv) != 0)
       return fail(BIV_EUNSUPPORTED, "attn_decode_bi: bf16 path needs Hq/Hkv dividing 32 (got %d)", Hq / Hkv);
-    return launch_attn_bf16("attn_decode_bi", q, q_stride, k_cache, v_cache, block_table, ctx, out, R, q_len, Hq, Hkv,
+    return launch_attn_bf16("attn_decode_bi", q, q_stride, k_cache, v_cache, block_table, ctx, q_off, out, R, q_len, Hq, Hkv,
                             max_blocks, num_blocks, scale, BIV_ATTN_SEG_TOKENS, true, workspace, workspace_bytes, s);
   }
   if (D != 64 && D != 128) return fail(BIV_EUNSUPPORTED, "attn_decode_bi: fp32 path supports D in {64,128} (D=%d)", D);
   hipLaunchKernelGGL(attn_f32_kernel, dim3(q_len, Hq, R), dim3(64), 0, s, static_cast<const float*>(q), q_stride,
-                     static_cast<const float*>(k_cache), static_cast<const float*>(v_cache), block_table, ctx,
+                     static_cast<const float*>(k_cache), static_cast<const float*>(v_cache), block_table, ctx, q_off,
                      static_cast<float*>(out), q_len, Hq, Hkv, D, max_blocks, num_blocks, scale);
   return launched("attn_decode_bi/f32");
 }
@@ -884,7 +910,8 @@ extern "C" biv_status attn_decode_adaptive(const void* q, int64_t q_stride, cons
   if (32 % (Hq / Hkv) != 0) return fail(BIV_EUNSUPPORTED, "attn_decode_adaptive: needs Hq/Hkv dividing 32");
   BIV_REQUIRE(split_tokens >= 0 && split_tokens % kChunk == 0, "attn_decode_adaptive: split_tokens must be a multiple of %d", kChunk);
   const int split = split_tokens == 0 ? biv_attn_adaptive_split(R, Hkv, max_blocks) : split_tokens;
-  return launch_attn_bf16("attn_decode_adaptive", q, q_stride, k_cache, v_cache, block_table, ctx, out, R, q_len, Hq, Hkv,
+  return launch_attn_bf16("attn_decode_adaptive", q, q_stride, k_cache, v_cache, block_table, ctx, nullptr, out, R, q_len, Hq, Hkv,
                           max_blocks, num_blocks, scale, split, false, workspace, workspace_bytes,
                           static_cast<hipStream_t>(stream));
 }
+

@@ -493,6 +493,27 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ partial, void* C,
   }
 }
 
+// The same second pass with SwiGLU applied (the gate/up weight interleaved in
+// blocks of 32 rows, as for gemm_bi's BIV_EPI_SWIGLU): output (m, j) sums
+// packed columns 64(j/32) + j%32 (gate) and that + 32 (up) over the splits,
+// then silu(g) * u, rounded once.
+template <int OUT_DT>
+__global__ void splitk_reduce_swiglu_kernel(const float* __restrict__ partial, void* C, int64_t M, int64_t N,
+                                            int splits) {
+  const int64_t n_out = N >> 1, MN = M * N;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < M * n_out; e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = e / n_out, j = e - m * n_out;
+    const int64_t cg = m * N + 64 * (j >> 5) + (j & 31), cu = cg + 32;
+    float g = partial[cg], u = partial[cu];
+    for (int k = 1; k < splits; ++k) {
+      g = __fadd_rn(g, partial[(int64_t)k * MN + cg]);
+      u = __fadd_rn(u, partial[(int64_t)k * MN + cu]);
+    }
+    const float act = __fdiv_rn(g, __fadd_rn(1.0f, expf(-g)));
+    store_from_f32(C, e, __fmul_rn(act, u), OUT_DT);
+  }
+}
+
 template <int OUT_DT, int EPI, bool kSplit>
 static void launch_bf16(const void* A, const void* B, void* C, float* partial, int M, int N, int K, int splits,
                         int k_per_split, hipStream_t s) {
@@ -569,39 +590,40 @@ constexpr int kSmallRows = 64;
 static_assert(wave_cols<BIV_GEMM_L32_TILE>() == kGumbelGroup && wave_cols<BIV_GEMM_L64_TILE>() == kGumbelGroup,
               "the Gumbel epilogue's group width is the L tile's columns per wave at every row count");
 
-template <int OUT_DT, int EPI>
+// kSplit: the split-K comparison path on the same small tiles (k ranges of
+// k_per_split, a multiple of 64).
+template <int OUT_DT, int EPI, bool kSplit = false>
 static void launch_dma_small(DmaTile t, const void* A, const void* B, void* C, float* partial, int M, int N, int K,
-                             hipStream_t s) {
+                             hipStream_t s, int splits = 1, int k_per_split = 0) {
   const bool r32 = M <= 32;
+  const int kps = kSplit ? k_per_split : K;
   if constexpr (EPI == BIV_EPI_SWIGLU || EPI == kEpiGumbel) {  // these epilogues run the L tile only
     (void)t;
-    if (r32) launch_dma_t<BIV_GEMM_L32_TILE, OUT_DT, EPI, false>(A, B, C, partial, M, N, K, 1, K, s);
-    else launch_dma_t<BIV_GEMM_L64_TILE, OUT_DT, EPI, false>(A, B, C, partial, M, N, K, 1, K, s);
+    if (r32) launch_dma_t<BIV_GEMM_L32_TILE, OUT_DT, EPI, kSplit>(A, B, C, partial, M, N, K, splits, kps, s);
+    else launch_dma_t<BIV_GEMM_L64_TILE, OUT_DT, EPI, kSplit>(A, B, C, partial, M, N, K, splits, kps, s);
   } else if (t == kTileL) {
-    if (r32) launch_dma_t<BIV_GEMM_L32_TILE, OUT_DT, EPI, false>(A, B, C, partial, M, N, K, 1, K, s);
-    else launch_dma_t<BIV_GEMM_L64_TILE, OUT_DT, EPI, false>(A, B, C, partial, M, N, K, 1, K, s);
+    if (r32) launch_dma_t<BIV_GEMM_L32_TILE, OUT_DT, EPI, kSplit>(A, B, C, partial, M, N, K, splits, kps, s);
+    else launch_dma_t<BIV_GEMM_L64_TILE, OUT_DT, EPI, kSplit>(A, B, C, partial, M, N, K, splits, kps, s);
   } else if (t == kTileQ) {
     // the 64-row tiles at every M <= 64: their two waves along M issue the
     // copies twice as fast as the 32-row tile's single wave (QKV at M = 1:
     // 45.7 us with 32 rows, 38.3 us with 64)
-    if (K % 128 == 0)
-      launch_dma_t<BIV_GEMM_Q64R_TILE, OUT_DT, EPI, false, 128>(A, B, C, partial, M, N, K, 1, K, s);
+    if (!kSplit && K % 128 == 0)
+      launch_dma_t<BIV_GEMM_Q64R_TILE, OUT_DT, EPI, kSplit, 128>(A, B, C, partial, M, N, K, splits, kps, s);
     else
-      launch_dma_t<BIV_GEMM_Q64K64_TILE, OUT_DT, EPI, false>(A, B, C, partial, M, N, K, 1, K, s);
+      launch_dma_t<BIV_GEMM_Q64K64_TILE, OUT_DT, EPI, kSplit>(A, B, C, partial, M, N, K, splits, kps, s);
   } else {  // S and T: 64 columns, two waves along N
-    if (r32) launch_dma_t<BIV_GEMM_N32_TILE, OUT_DT, EPI, false>(A, B, C, partial, M, N, K, 1, K, s);
-    else launch_dma_t<BIV_GEMM_N64_TILE, OUT_DT, EPI, false>(A, B, C, partial, M, N, K, 1, K, s);
+    if (r32) launch_dma_t<BIV_GEMM_N32_TILE, OUT_DT, EPI, kSplit>(A, B, C, partial, M, N, K, splits, kps, s);
+    else launch_dma_t<BIV_GEMM_N64_TILE, OUT_DT, EPI, kSplit>(A, B, C, partial, M, N, K, splits, kps, s);
   }
 }
 
 template <int OUT_DT, int EPI, bool kSplit>
 static void launch_dma(DmaTile t, const void* A, const void* B, void* C, float* partial, int M, int N, int K,
                        int splits, int k_per_split, hipStream_t s) {
-  if constexpr (!kSplit) {
-    if (M <= kSmallRows) {
-      launch_dma_small<OUT_DT, EPI>(t, A, B, C, partial, M, N, K, s);
-      return;
-    }
+  if (M <= kSmallRows) {
+    launch_dma_small<OUT_DT, EPI, kSplit>(t, A, B, C, partial, M, N, K, s, splits, k_per_split);
+    return;
   }
   if (t == kTileL)
     launch_dma_t<BIV_GEMM_L_TILE, OUT_DT, EPI, kSplit>(A, B, C, partial, M, N, K, splits, k_per_split, s);
@@ -703,13 +725,39 @@ extern "C" biv_status gemm_bi(const void* A, const void* B, void* C, int64_t M, 
 }
 
 namespace biv {
-// Split count chosen the way a throughput-oriented library would: enough
-// workgroups for two per compute unit, each split at least two K tiles.
+// Tiles of the staged kernel's grid for an (M, N) output: the column tiling
+// of N's weight class, and its rows per tile (32 or 64 at M <= 64).
+static int64_t staged_tiles(int64_t M, int64_t N) {
+  int64_t bm, bn;
+  switch (dma_tile_for(N)) {
+    case kTileL: bm = 256; bn = 256; break;
+    case kTileQ: bm = 128; bn = 96; break;
+    default: bm = 128; bn = 64; break;
+  }
+  if (M <= kSmallRows) bm = M <= 32 && dma_tile_for(N) != kTileQ ? 32 : 64;
+  return cdiv(M, bm) * cdiv(N, bn);
+}
+
+// Split count of gemm_splitk's automatic choice: double it while the staged
+// kernel's grid holds fewer workgroups than the GPU has compute units (one
+// workgroup per CU is what these tiles run at), up to 8 and while every
+// split keeps at least four 64-wide k stages.  1 means no split: the plain
+// staged kernel, with no partial sums or second pass.
 static int auto_splits(int64_t M, int64_t N, int64_t K) {
-  const int64_t tiles = cdiv(M, kBM) * cdiv(N, kBN);
-  int64_t s = cdiv(512, tiles);
-  s = std::min<int64_t>(s, std::max<int64_t>(1, K / (2 * kBK)));
-  return (int)std::max<int64_t>(1, std::min<int64_t>(s, 64));
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) ==
+                                                  hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  if (K % kDBK != 0) return std::max<int64_t>(1, std::min<int64_t>(cdiv(2 * cus, cdiv(M, kBM) * cdiv(N, kBN)), 8));
+  const int64_t tiles = staged_tiles(M, N);
+  int s = 1;
+  while (s < 8 && tiles * s < cus && K / (2 * s) >= 4 * kDBK) s *= 2;
+  return s;
 }
 static int split_len(int64_t K, int splits) { return (int)(cdiv(cdiv(K, splits), kBK) * kBK); }
 }  // namespace biv
@@ -732,16 +780,21 @@ extern "C" biv_status gemm_splitk(const void* A, const void* B, void* C, int64_t
   using namespace biv;
   biv_status st = check_gemm_args("gemm_splitk", A, B, C, M, N, K, out_dt, epilogue);
   if (st != BIV_OK) return st;
-  BIV_REQUIRE(epilogue != BIV_EPI_SWIGLU, "gemm_splitk: no SwiGLU epilogue (use swiglu() on the packed product)");
+  BIV_REQUIRE(epilogue != BIV_EPI_SWIGLU || (N % 64 == 0 && K % kDBK == 0),
+              "gemm_splitk: the SwiGLU epilogue needs N %% 64 == 0 and K %% 64 == 0");
   BIV_REQUIRE(splits >= 0 && splits <= 64, "gemm_splitk: splits must be in [0, 64]");
   if (M == 0) return BIV_OK;
   BIV_REQUIRE(K % 8 == 0 && aligned16(A) && aligned16(B), "gemm_splitk: needs K %% 8 == 0 and aligned A, B");
   int sp = splits == 0 ? auto_splits(M, N, K) : splits;
   const int kps = split_len(K, sp);
   sp = (int)cdiv(K, kps);  // drop empty splits
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (sp == 1) {  // no split: the invariant kernel itself, no partials
+    const biv_status st1 = gemm_bi(A, B, C, M, N, K, BIV_BF16, out_dt, epilogue, stream);
+    return st1;
+  }
   BIV_REQUIRE(workspace != nullptr && workspace_bytes >= biv_splitk_workspace_bytes(M, N, sp),
               "gemm_splitk: workspace needs %zu bytes", biv_splitk_workspace_bytes(M, N, sp));
-  hipStream_t s = static_cast<hipStream_t>(stream);
   float* part = static_cast<float*>(workspace);
   if (K % kDBK == 0)
     launch_dma<BIV_F32, BIV_EPI_STORE, true>(dma_tile_for(N), A, B, C, part, (int)M, (int)N, (int)K, sp, kps, s);
@@ -751,6 +804,11 @@ extern "C" biv_status gemm_splitk(const void* A, const void* B, void* C, int64_t
   if (st != BIV_OK) return st;
   const int64_t MN = M * N;
   const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(MN, 256), 16384);
+  if (epilogue == BIV_EPI_SWIGLU) {
+    if (out_dt == BIV_BF16) hipLaunchKernelGGL((splitk_reduce_swiglu_kernel<BIV_BF16>), dim3(blocks), dim3(256), 0, s, part, C, M, N, sp);
+    else hipLaunchKernelGGL((splitk_reduce_swiglu_kernel<BIV_F32>), dim3(blocks), dim3(256), 0, s, part, C, M, N, sp);
+    return launched("gemm_splitk/reduce-swiglu");
+  }
   if (out_dt == BIV_BF16) {
     if (epilogue == BIV_EPI_ACCUM) hipLaunchKernelGGL((splitk_reduce_kernel<BIV_BF16, BIV_EPI_ACCUM>), dim3(blocks), dim3(256), 0, s, part, C, MN, sp);
     else hipLaunchKernelGGL((splitk_reduce_kernel<BIV_BF16, BIV_EPI_STORE>), dim3(blocks), dim3(256), 0, s, part, C, MN, sp);

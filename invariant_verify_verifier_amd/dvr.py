@@ -12,8 +12,8 @@ token wherever their logits agree closely enough, and the committed stream is
 the stream the invariant kernels would produce one token at a time.
 
 Here the fast path runs the same decoder with split-K GEMMs
-(``gemm_splitk``, splits chosen from the shape) and load-adaptive attention
-splits (``attn_decode_adaptive``), one token per request per forward.  Noise
+(``gemm_splitk``) and load-adaptive attention splits
+(``attn_decode_adaptive``), one token per request per forward.  Noise
 comes from a caller-supplied function of (requests, positions), prepared in
 advance like the verifier's.  Everything runs through the HIP library; the
 host only moves the K sampled tokens and the accepted lengths.
@@ -29,35 +29,96 @@ from . import _lib as L
 from . import verifier as V
 
 
+def _event_ms(fn, iters=5, warmup=2):
+    for _ in range(warmup):
+        fn()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(iters):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / iters
+
+
 class SplitKernels:
     """The decoder's GEMMs and attention swapped for their non-invariant
-    counterparts: split-K with the split count chosen from (M, N, K)
-    (``gemm_splitk``, auto) and attention with the KV split chosen from the
-    load (``attn_decode_adaptive``, auto).  Owns its workspaces; pass
-    ``gemm_fn=sk.gemm, attn_fn=sk.attn`` to ``VerifierModel.forward``."""
+    counterparts: split-K GEMMs (``gemm_splitk``) and attention whose KV split
+    follows the load (``attn_decode_adaptive``).  Owns its workspaces; pass
+    ``gemm_fn=sk.gemm, attn_fn=sk.attn`` to ``VerifierModel.forward``.
 
-    def __init__(self, R, Hkv, max_blocks, device="cuda"):
-        self.device = device
+    tune=False: the library's automatic choices (splits from the staged
+    kernel's own grid; the attention split from the batch).  tune=True: the
+    first call of each shape times the candidates -- 1, 2, 4 and 8 splits
+    (1 is the invariant kernel itself), KV splits of 256 * 2^k tokens up to
+    the longest context -- into scratch outputs and keeps the fastest, as a
+    serving engine tuned for speed rather than invariance would.  The tuning
+    runs eagerly (never inside a graph capture)."""
+
+    GEMM_SPLITS = (1, 2, 4, 8)
+
+    def __init__(self, R, Hkv, max_blocks, device="cuda", tune=False):
+        self.device, self.tune = device, tune
+        self.max_blocks = max_blocks
         self.split = L.attn_adaptive_split(R, Hkv, max_blocks)
-        self.attn_ws = torch.empty(max(L.attn_workspace_bytes(R, Hkv, max_blocks, self.split), 16),
+        self.attn_splits = {}
+        self.attn_ws = torch.empty(max(L.attn_workspace_bytes(R, Hkv, max_blocks, 256 if tune else self.split), 16),
                                    dtype=torch.uint8, device=device)
         self.gemm_ws = {}
         self.splits = {}
+        self.timings = {}
 
-    def gemm(self, a, b, c, accumulate=False):
-        M, K = a.shape
-        N = b.shape[0]
-        sp = L.splitk_auto_splits(M, N, K)
-        self.splits[(N, K)] = sp
+    def _ws(self, M, N, sp):
         ws = self.gemm_ws.get((M, N, sp))
         if ws is None:
             ws = torch.empty(max(L.splitk_workspace_bytes(M, N, sp), 16), dtype=torch.uint8, device=self.device)
             self.gemm_ws[(M, N, sp)] = ws
-        return L.gemm_splitk(a, b, c, sp, ws, accumulate=accumulate)
+        return ws
+
+    def _choose_splits(self, a, b, c, accumulate, swiglu):
+        M, K = a.shape
+        N = b.shape[0]
+        key = (M, N, K)
+        if key not in self.splits:
+            if not self.tune:
+                self.splits[key] = L.splitk_auto_splits(M, N, K)
+            else:
+                scratch = torch.zeros_like(c)
+                t = {sp: _event_ms(lambda sp=sp: L.gemm_splitk(a, b, scratch, sp, self._ws(M, N, sp),
+                                                               accumulate=accumulate, swiglu=swiglu))
+                     for sp in self.GEMM_SPLITS if K % (64 * sp) == 0}
+                self.timings[("gemm", M, N, K)] = {sp: round(ms * 1e3, 2) for sp, ms in t.items()}
+                self.splits[key] = min(t, key=t.get)
+        return self.splits[key]
+
+    def gemm(self, a, b, c, accumulate=False, swiglu=False):
+        M, K = a.shape
+        N = b.shape[0]
+        sp = self._choose_splits(a, b, c, accumulate, swiglu)
+        return L.gemm_splitk(a, b, c, sp, self._ws(M, N, sp), accumulate=accumulate, swiglu=swiglu)
 
     def attn(self, q, k_cache, v_cache, block_table, ctx, out, q_len, scale, workspace=None):
+        split = self.split
+        if self.tune:
+            key = (block_table.shape[0], q_len)
+            if key not in self.attn_splits:
+                scratch = torch.empty_like(out)
+                cands, sp = [], 256
+                while True:
+                    cands.append(sp)
+                    if sp >= self.max_blocks * 16:
+                        break
+                    sp *= 2
+                t = {sp: _event_ms(lambda sp=sp: L.attn_decode_adaptive(q, k_cache, v_cache, block_table, ctx,
+                                                                        scratch, q_len, scale, self.attn_ws,
+                                                                        split_tokens=sp))
+                     for sp in cands}
+                self.timings[("attn",) + key] = {sp: round(ms * 1e3, 2) for sp, ms in t.items()}
+                self.attn_splits[key] = min(t, key=t.get)
+            split = self.attn_splits[key]
         return L.attn_decode_adaptive(q, k_cache, v_cache, block_table, ctx, out, q_len, scale, self.attn_ws,
-                                      split_tokens=self.split)
+                                      split_tokens=split)
 
 
 @dataclass

@@ -166,8 +166,8 @@ class VerifierModel:
             attend(qkv[:, :qc], k_cache, v_cache, block_table, ctx, attn, q_len, scale, ws)
             gemm(attn.view(W, qc), lw["wo"], x, accumulate=True)
             L.rmsnorm_bi(x, lw["ffn_norm"], h, sh.eps)
-            if gemm_fn is None and self.dtype == torch.bfloat16:
-                L.gemm_bi(h, lw["w_gu"], act, swiglu=True)
+            if self.dtype == torch.bfloat16:  # SwiGLU in the matmul's epilogue
+                gemm(h, lw["w_gu"], act, swiglu=True)
             else:
                 gemm(h, lw["w_gu"], gu)
                 L.swiglu(gu, act, block=L.SWIGLU_BLOCK)

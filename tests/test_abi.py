@@ -58,8 +58,16 @@ def test_host_side_argument_errors(lib):
     assert lib.gemm_bi(bp, bp, bp, 4, 96, 64, 1, 1, 2, None) == 1  # SwiGLU epilogue: N % 64 != 0
     assert lib.gemm_bi(bp, bp, bp, 4, 128, 64, 0, 0, 2, None) == 1  # SwiGLU epilogue: fp32 inputs
     assert lib.gemm_bi(bp, bp, bp, 4, 128, 64, 1, 1, 3, None) == 1  # unknown epilogue
-    lib.rmsnorm_bi.argtypes = [vp, i32, vp, vp, i32, i64, i64, f32, vp]
-    assert lib.rmsnorm_bi(None, 0, None, None, 0, 3, 0, 1e-6, None) == 1
+    lib.rmsnorm_bi.argtypes = [vp, i32, vp, vp, vp, i32, i64, i64, f32, vp]
+    assert lib.rmsnorm_bi(None, 0, None, None, None, 0, 3, 0, 1e-6, None) == 1  # H = 0
+    assert lib.rmsnorm_bi(None, 0, None, None, None, 0, 0, 8, 1e-6, None) == 0  # M = 0: nothing to do
+    big = ctypes.create_string_buffer(1 << 16)
+    b0 = ctypes.cast(big, vp).value
+    # x and y overlap; residual overlapping x (4 rows of 64 fp32 = 1 KiB each)
+    assert lib.rmsnorm_bi(b0, 0, None, b0 + 8192, b0 + 512, 0, 4, 64, 1e-6, None) == 1
+    assert b"overlap" in lib.biv_last_error()
+    assert lib.rmsnorm_bi(b0, 0, b0 + 512, b0 + 8192, b0 + 16384, 0, 4, 64, 1e-6, None) == 1
+    assert b"overlap" in lib.biv_last_error()
     lib.gumbel_verify.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, vp, vp]
     assert lib.gumbel_verify(None, None, None, 2, 0, 8, None, None, None, None) == 1  # K = 0
     assert lib.gumbel_verify(None, None, None, 0, 4, 8, None, None, None, None) == 0  # R = 0
@@ -85,18 +93,22 @@ def test_host_side_argument_errors(lib):
     assert lib.rope_kv_overwrite(bp, 6000, bp, bp, bp, bp, bp, 1, 32, 8, 128, 16, 4, 1, None) == 1
     assert lib.rope_kv_overwrite(bp, 6144, bp, bp, bp, bp, bp, 1, 32, 8, 127, 16, 4, 1, None) == 1  # odd D
     assert lib.rope_kv_overwrite(None, 6144, None, None, None, None, None, 0, 32, 8, 128, 16, 4, 1, None) == 0
-    lib.attn_decode_bi.argtypes = [vp, i64, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp,
+    lib.attn_decode_bi.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp,
                                    ctypes.c_size_t, vp]
     # Hq not a multiple of Hkv
-    assert lib.attn_decode_bi(None, 4096, None, None, None, None, None, 1, 1, 30, 8, 128, 4, 4, 0.1, 1, None, 0,
+    assert lib.attn_decode_bi(None, 4096, None, None, None, None, None, None, 1, 1, 30, 8, 128, 4, 4, 0.1, 1, None, 0,
                               None) == 1
     # bf16 path: G = Hq/Hkv must divide 32 (unsupported otherwise, not invalid); q_len * G > 32 takes
     # several row blocks and a workspace sized for them
     buf = ctypes.create_string_buffer(64)
     p = ctypes.cast(buf, vp)
-    assert lib.attn_decode_bi(p, 4096, p, p, p, p, p, 1, 16, 24, 8, 128, 4, 4, 0.1, 1, p, 64, None) == 2
-    assert lib.attn_decode_bi(p, 4096, p, p, p, p, p, 1, 16, 32, 8, 128, 4, 4, 0.1, 1, p, 64, None) == 1
+    assert lib.attn_decode_bi(p, 4096, p, p, p, p, None, p, 1, 16, 24, 8, 128, 4, 4, 0.1, 1, p, 64, None) == 2
+    assert lib.attn_decode_bi(p, 4096, p, p, p, p, None, p, 1, 16, 32, 8, 128, 4, 4, 0.1, 1, p, 64, None) == 1
     assert b"workspace" in lib.biv_last_error()
+    # with row offsets the workspace is sized by q_len, the most rows of any request
+    assert lib.attn_decode_bi(p, 4096, p, p, p, p, p, p, 2, 16, 32, 8, 128, 4, 4, 0.1, 1, p, 64, None) == 1
+    assert b"workspace" in lib.biv_last_error()
+    assert lib.attn_decode_bi(p, 4096, p, p, p, p, p, p, 0, 16, 32, 8, 128, 4, 4, 0.1, 1, None, 0, None) == 0
     lib.biv_attn_workspace_bytes_q.restype = ctypes.c_size_t
     lib.biv_attn_workspace_bytes_q.argtypes = [ctypes.c_int] * 6
     lib.biv_attn_workspace_bytes.restype = ctypes.c_size_t
@@ -107,6 +119,11 @@ def test_host_side_argument_errors(lib):
     assert lib.biv_attn_workspace_bytes_q(3, 8, 24, 8, 40, 2048) == 0
 
 
+def test_abi_version(lib):
+    lib.biv_abi_version.restype = ctypes.c_int
+    assert lib.biv_abi_version() == 2
+
+
 def test_workspace_sizes(lib):
     lib.biv_attn_workspace_bytes.restype = ctypes.c_size_t
     lib.biv_attn_workspace_bytes.argtypes = [ctypes.c_int] * 4
@@ -115,8 +132,14 @@ def test_workspace_sizes(lib):
     assert n == 64 * 8 * nseg * (4096 + 128) * 4 + 64 * nseg * 4  # segment results + work list
     lib.biv_splitk_auto_splits.restype = ctypes.c_int
     lib.biv_splitk_auto_splits.argtypes = [ctypes.c_int64] * 3
-    assert lib.biv_splitk_auto_splits(1, 14336, 4096) > 1  # small M -> split K
-    assert lib.biv_splitk_auto_splits(512, 14336, 4096) == 2
+    # the staged kernel's own grid: M = 1 on a 14336-wide weight is 224 tiles of
+    # 32 x 64 (fewer than 256 CUs) -> 2 splits; M = 512 already fills the GPU -> 1
+    assert lib.biv_splitk_auto_splits(1, 14336, 4096) == 2
+    assert lib.biv_splitk_auto_splits(1, 4096, 14336) == 4  # 64 tiles
+    assert lib.biv_splitk_auto_splits(512, 14336, 4096) == 1
+    assert lib.biv_splitk_auto_splits(512, 4096, 4096) == 1  # 256 tiles of 128 x 64
+    assert lib.biv_splitk_auto_splits(1, 4096, 512) == 2  # every split keeps >= 4 k stages of 64
+    assert lib.biv_splitk_auto_splits(1, 4096, 256) == 1
 
 
 def test_rope_table_host_values(lib):

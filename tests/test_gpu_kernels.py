@@ -16,7 +16,7 @@ import torch
 import oracle
 import workloads as wl
 from gpu_util import DEV, announce, bits, dev_bf16, dev_f32, dev_i32, dev_i64, f64, sync
-from tolerances import check_bf16, check_f32
+from tolerances import bf16_step, check_bf16, check_f32
 
 pytestmark = pytest.mark.gpu
 
@@ -373,7 +373,8 @@ def test_rmsnorm_vector_path_f32_residual(biv, H):
         biv.rmsnorm_bi(x[:M].contiguous(), dev_bf16(gb), yM, 1e-6)
         sync()
         assert np.array_equal(bits(yM), full[:M]), f"rows changed at M={M}"
-    # misaligned rows (offset by one element) -> scalar path
+    # misaligned rows (offset by one element) -> the scalar kernel, which owns
+    # and adds the same elements in the same order: the same bits
     buf = torch.empty(Mx * H + 1, dtype=torch.float32, device=DEV)
     xm = buf[1:].view(Mx, H)
     xm.copy_(x)
@@ -381,6 +382,66 @@ def test_rmsnorm_vector_path_f32_residual(biv, H):
     biv.rmsnorm_bi(xm, dev_bf16(gb), ym, 1e-6)
     sync()
     check_bf16(f64(ym), oracle.rmsnorm(x_np.astype(np.float64), oracle.as_f64(gb, "bf16"), 1e-6), "rmsnorm misaligned")
+    assert np.array_equal(bits(ym), full), "misaligned x and y changed the bits"
+    # only the output misaligned, or only gamma: the same bits again
+    yo = torch.empty(Mx * H + 1, dtype=torch.bfloat16, device=DEV)[1:].view(Mx, H)
+    biv.rmsnorm_bi(x, dev_bf16(gb), yo, 1e-6)
+    gm = torch.empty(H + 1, dtype=torch.bfloat16, device=DEV)[1:]
+    gm.copy_(dev_bf16(gb))
+    yg = torch.empty((Mx, H), dtype=torch.bfloat16, device=DEV)
+    biv.rmsnorm_bi(x, gm, yg, 1e-6)
+    sync()
+    assert np.array_equal(bits(yo), full), "a misaligned output changed the bits"
+    assert np.array_equal(bits(yg), full), "a misaligned gamma changed the bits"
+
+
+@pytest.mark.parametrize("dt,H,M", [("bf16", 4096, 300), ("f32", 4096, 37), ("bf16", 1000, 19), ("f32", 2048, 5)])
+def test_rmsnorm_fused_residual(biv, dt, H, M):
+    """rmsnorm_bi with a residual: s = x + residual stored back (rounded once to
+    the activation dtype), y = rmsnorm(s).  Against the oracle: s is the exact
+    sum rounded once (within one rounding of it), y is the fp64 norm of the
+    stored s; bitwise equal to adding first and normalising s alone, and row
+    bits independent of M and of the vector/scalar kernel."""
+    if dt == "bf16":
+        xb, rb = wl.normal_bf16(60 + H, (M, H)), wl.normal_bf16(61 + H, (M, H), std=3.0)
+        x64, r64 = oracle.as_f64(xb, "bf16"), oracle.as_f64(rb, "bf16")
+        x, r = dev_bf16(xb), dev_bf16(rb)
+        s_ref = oracle.round_bf16(x64 + r64)
+    else:
+        xf, rf = wl.normal_f32(60 + H, (M, H)), wl.normal_f32(61 + H, (M, H), std=3.0)
+        x64, r64 = xf.astype(np.float64), rf.astype(np.float64)
+        x, r = dev_f32(xf), dev_f32(rf)
+        s_ref = (x64 + r64).astype(np.float32).astype(np.float64)
+    gb = wl.normal_bf16(62 + H, (H,), std=0.1, mean=1.0)
+    g64 = oracle.as_f64(gb, "bf16")
+    gam = dev_bf16(gb)
+    announce("rmsnorm fused residual", dt, H, M)
+    res = r.clone()
+    y = torch.empty((M, H), dtype=torch.bfloat16, device=DEV)
+    biv.rmsnorm_bi(x, gam, y, 1e-6, residual=res)
+    sync()
+    s_gpu = f64(res)
+    if dt == "bf16":  # one fp32 add of two bf16 values, then one rounding to bf16: at most one step apart
+        assert np.all(np.abs(s_gpu - s_ref) <= bf16_step(s_ref))
+        assert np.mean(s_gpu == s_ref) > 0.9999
+    else:
+        assert np.array_equal(s_gpu, s_ref), "fp32 residual add is one IEEE add"
+    check_bf16(f64(y), oracle.rmsnorm(s_gpu, g64, 1e-6), "rmsnorm of the stored residual")
+    check_bf16(f64(y), oracle.rmsnorm(x64 + r64, g64, 1e-6), "rmsnorm of the exact sum")
+    # fused == add, then normalise the stored sum with no residual
+    y2 = torch.empty_like(y)
+    biv.rmsnorm_bi(res.clone(), gam, y2, 1e-6)
+    sync()
+    assert np.array_equal(bits(y2), bits(y))
+    # M-invariance of the fused call
+    full = bits(y)
+    for m in (1, M // 2 + 1):
+        rm = r[:m].clone()
+        ym = torch.empty((m, H), dtype=torch.bfloat16, device=DEV)
+        biv.rmsnorm_bi(x[:m].contiguous(), gam, ym, 1e-6, residual=rm)
+        sync()
+        assert np.array_equal(bits(ym), full[:m]) and np.array_equal(bits(rm), bits(res)[:m])
+
 
 
 # =====================================================================
@@ -518,6 +579,37 @@ def test_gemm_bf16_tile_classes_invariance(biv, N):
         biv.gemm_bi(a[:M].contiguous(), w, cM)
         sync()
         assert np.array_equal(bits(cM), full_bits[:M]), f"rows changed at M={M}, N={N}"
+
+
+def test_gemm_bf16_down_projection_shape(biv):
+    """The pass's longest reduction: the down projection [M, 14336] x
+    [4096, 14336]^T (224 k-stages of 64) with the residual-accumulate
+    epilogue into an fp32 stream, as the decoder calls it.  Parity with the
+    oracle (fp32 output, per-row relative bound) at M = 512, and every row's
+    bits the same at M = 1, 7, 32, 33, 64, 65 (the 32- and 64-row tiles) as
+    inside M = 512 (the 128-row tile)."""
+    M, N, K = 512, 4096, 14336
+    a_np = wl.normal_bf16(190, (M, K), std=1.0)
+    w_np = wl.normal_bf16(191, (N, K), std=0.02)
+    r_np = wl.normal_f32(192, (M, N), std=3.0)
+    a, w = dev_bf16(a_np), dev_bf16(w_np)
+    announce("gemm bf16 down projection shape", M, N, K)
+    full = dev_f32(r_np)
+    biv.gemm_bi(a, w, full, accumulate=True)
+    sync()
+    ref = r_np.astype(np.float64) + oracle.linear(oracle.as_f64(a_np, "bf16"), oracle.as_f64(w_np, "bf16"))
+    check_f32(f64(full), ref, axis=1, what="down projection + residual")
+    full_bits = bits(full)
+    for m in (1, 7, 32, 33, 64, 65):
+        cm = dev_f32(r_np[:m])
+        biv.gemm_bi(a[:m].contiguous(), w, cm, accumulate=True)
+        sync()
+        assert np.array_equal(bits(cm), full_bits[:m]), f"rows changed at M={m}"
+    # bf16 output of the same product (store epilogue): R16 bf16 bound
+    cb = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    biv.gemm_bi(a, w, cb)
+    sync()
+    check_bf16(f64(cb), ref - r_np.astype(np.float64), "down projection bf16 out")
 
 
 @pytest.mark.parametrize("K", [4096, 4160])
@@ -738,6 +830,53 @@ def test_attention_bf16_row_blocks_prefill(biv, q_len, G):
                                   num_blocks=lay.num_blocks, max_blocks=lay.max_blocks)
             one = bits(_run_attn(biv, lay1, kc, vc, q[r * q_len + j:r * q_len + j + 1], 1))
             assert np.array_equal(one[0], full[r * q_len + j]), f"request {r} row {j}"
+
+
+def _ragged_case(biv, ctx, qlens, Hq, Hkv, D, seed, dtype="bf16"):
+    """Requests with their own row counts (q_off), laid out back to back; returns
+    (layout, caches, q, offsets, output bits, output values)."""
+    qmax = max(qlens)
+    lay = wl.paged_layout(ctx, qmax, seed=seed, spare_blocks=2)
+    mk = wl.normal_bf16 if dtype == "bf16" else wl.normal_f32
+    kc = mk(seed + 1, (lay.num_blocks, Hkv, 16, D))
+    vc = mk(seed + 2, (lay.num_blocks, Hkv, 16, D))
+    off = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    q = mk(seed + 3, (int(off[-1]), Hq, D))
+    out = _run_attn(biv, lay, kc, vc, q, qmax, dtype=dtype, q_off=dev_i32(off))
+    return lay, kc, vc, q, off, bits(out), f64(out)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_attention_ragged_rows_q_off(biv, dtype):
+    """attn_decode_bi with per-request row offsets (requests bring different
+    numbers of candidates, one none): every request's rows match the oracle and
+    equal, bit for bit, that request run alone with a uniform q_len; a
+    request's rows do not change when its neighbours' row counts change."""
+    Hq, Hkv, D = (32, 8, 128) if dtype == "bf16" else (4, 4, 64)
+    ctx = [700, 4090, 0, 2500, 9000, 300]
+    qlens = [1, 8, 5, 20, 0, 3]  # 20 rows at G = 4: three 8-position row blocks
+    announce("attention ragged rows", dtype, qlens)
+    lay, kc, vc, q, off, ob, ov = _ragged_case(biv, ctx, qlens, Hq, Hkv, D, seed=170, dtype=dtype)
+    chk = (lambda g, r, w: check_bf16(g, r, w)) if dtype == "bf16" else (lambda g, r, w: check_f32(g, r, what=w))
+    for r, n in enumerate(qlens):
+        if n == 0:
+            continue
+        rows = q[off[r]:off[r + 1]]
+        lay1 = wl.PagedLayout(ctx=np.array([ctx[r]], np.int32), q_len=n, block_table=lay.block_table[r:r + 1],
+                              num_blocks=lay.num_blocks, max_blocks=lay.max_blocks)
+        chk(ov[off[r]:off[r + 1]], _attn_ref(lay1, kc, vc, rows, n, dtype), f"ragged request {r}")
+        alone = bits(_run_attn(biv, lay1, kc, vc, rows, n, dtype=dtype))
+        assert np.array_equal(ob[off[r]:off[r + 1]], alone), f"request {r} differs from running alone"
+    # the neighbours' row counts change (same caches and pages); request 3
+    # (20 rows) keeps its bits
+    qlens2 = [8, 2, 1, 20, 7, 8]
+    off2 = np.concatenate([[0], np.cumsum(qlens2)]).astype(np.int32)
+    mk = wl.normal_bf16 if dtype == "bf16" else wl.normal_f32
+    q2 = mk(180, (int(off2[-1]), Hq, D))
+    q2[off2[3]:off2[4]] = q[off[3]:off[4]]
+    announce("attention ragged rows, other neighbours", dtype, qlens2)
+    out2 = _run_attn(biv, lay, kc, vc, q2, max(qlens2), dtype=dtype, q_off=dev_i32(off2))
+    assert np.array_equal(bits(out2)[off2[3]:off2[4]], ob[off[3]:off[4]])
 
 
 def test_attention_f32_parity(biv):
