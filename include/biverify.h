@@ -211,6 +211,35 @@ biv_status attn_decode_bi(const void* q, int64_t q_stride, const void* k_cache, 
                           biv_dtype dt, void* workspace, size_t workspace_bytes, biv_stream stream);
 
 /* --------------------------------------------------------------------------
+ * attn_decode_bi_static — attn_decode_bi without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  It allocates
+ * nothing: the segment partials (and work list) go to a static array of
+ * BIV_ATTN_STATIC_SCRATCH_BYTES in the library's device code, one per GPU,
+ * held from the library's load until the process ends.  Arguments, results
+ * and bits are those of attn_decode_bi (same kernels).
+ *
+ * The call needs biv_attn_workspace_bytes_q(R, q_len, Hq, Hkv, max_blocks,
+ * BIV_ATTN_SEG_TOKENS) <= BIV_ATTN_STATIC_SCRATCH_BYTES (32 MiB) and returns
+ * BIV_EINVAL, launching nothing, when it needs more.  That covers, e.g., the
+ * verify step of 64 requests x 8 KV heads at contexts up to 12288 (26 MB) or
+ * one request up to 32768 (18 MB); batches small enough for their segments to be
+ * split over several waves reserve room for every 256-token chunk's partial
+ * (16 per segment) and reach the limit sooner.  Every call
+ * on a GPU shares that GPU's array (it keeps the last call's contents; the
+ * kernels need no initialisation), so calls that overlap on one GPU -- on two
+ * streams, or from two threads -- race: order them on one stream.  The
+ * array's address on a GPU is looked up at the first call there, with that
+ * GPU current (BIV_EHIP if the runtime cannot give it).
+ * ------------------------------------------------------------------------ */
+#define BIV_ATTN_STATIC_SCRATCH_BYTES (32u << 20)
+
+biv_status attn_decode_bi_static(const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_table, const int32_t* ctx, const int32_t* q_off, void* out,
+                                 int R, int q_len, int Hq, int Hkv, int D, int max_blocks, int num_blocks,
+                                 float scale, biv_dtype dt, biv_stream stream);
+
+/* --------------------------------------------------------------------------
  * gumbel_verify — Gumbel-max coupled verification ([GUMBEL]: add Gumbel(0,1)
  * noise to the logits and take the argmax; the same noise couples draft and
  * target, so verification compares the draft token with the target token).

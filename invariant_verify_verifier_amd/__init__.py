@@ -13,6 +13,8 @@ from ._lib import (  # noqa: F401
     attn_adaptive_split,
     attn_decode_adaptive,
     attn_decode_bi,
+    attn_decode_bi_static,
+    ATTN_STATIC_SCRATCH_BYTES,
     attn_workspace_bytes,
     embed_rows,
     exported_symbols,

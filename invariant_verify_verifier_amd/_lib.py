@@ -41,6 +41,8 @@ _SIGS = {
     "biv_attn_workspace_bytes_q": ([_i32, _i32, _i32, _i32, _i32, _i32], _sz),
     "attn_decode_bi": ([_vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                         _i32, _vp, _sz, _vp], _i32),
+    "attn_decode_bi_static": ([_vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                               _f32, _i32, _vp], _i32),
     "gumbel_verify": ([_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp], _i32),
     "gumbel_topk": ([_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp], _i32),
     "biv_gumbel_workspace_bytes": ([_i32, _i32], _sz),
@@ -220,6 +222,24 @@ def attn_decode_bi(q, k_cache, v_cache, block_table, ctx, out, q_len, scale, wor
     _check("attn_decode_bi", _lib.attn_decode_bi(
         _p(q), q_stride, _p(k_cache), _p(v_cache), _p(block_table), _p(ctx), _p(q_off), _p(out), R, q_len, Hq, Hkv, D,
         max_blocks, num_blocks, scale, _dt(q), _p(workspace), wbytes, _stream()))
+    return out
+
+
+ATTN_STATIC_SCRATCH_BYTES = 32 << 20
+
+
+def attn_decode_bi_static(q, k_cache, v_cache, block_table, ctx, out, q_len, scale, q_off=None):
+    """attn_decode_bi with its workspace in the library's static per-GPU
+    scratch (allocates nothing; for callers that cannot allocate).  Calls
+    whose workspace would exceed ATTN_STATIC_SCRATCH_BYTES raise; calls that
+    overlap on one GPU race (order them on one stream)."""
+    _contig(k_cache, v_cache, block_table, ctx, out, q_off)
+    q_stride, Hq, D = _attn_checks(q, k_cache, v_cache, block_table, ctx, out, q_len, q_off)
+    R, max_blocks = block_table.shape
+    num_blocks, Hkv = k_cache.shape[0], k_cache.shape[1]
+    _check("attn_decode_bi_static", _lib.attn_decode_bi_static(
+        _p(q), q_stride, _p(k_cache), _p(v_cache), _p(block_table), _p(ctx), _p(q_off), _p(out), R, q_len, Hq, Hkv, D,
+        max_blocks, num_blocks, scale, _dt(q), _stream()))
     return out
 
 

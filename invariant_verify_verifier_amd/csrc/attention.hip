@@ -36,6 +36,7 @@
 // and its position -- not on the batch, the other rows or the grid.  A chunk
 // or segment with no visible key for a row folds as an exact no-op.
 #include <algorithm>
+#include <mutex>
 
 #include "biv_internal.h"
 
@@ -915,3 +916,64 @@ extern "C" biv_status attn_decode_adaptive(const void* q, int64_t q_stride, cons
                           static_cast<hipStream_t>(stream));
 }
 
+// ----------------------------------------------------------------------------
+// attn_decode_bi_static: attn_decode_bi with its workspace in memory the
+// library holds, for callers that cannot allocate.  `scratch` is a file-scope
+// device array; in host code its name only stands in for the symbol, so its
+// device address on each GPU is looked up once (hipGetSymbolAddress, with
+// that GPU current, at the entry point's first call there) and only that
+// address is ever handed to a kernel.
+namespace biv {
+
+static __device__ __align__(256) unsigned char scratch[BIV_ATTN_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {nullptr};
+
+static biv_status static_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(BIV_EHIP, "attn_decode_bi_static: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(BIV_EUNSUPPORTED, "attn_decode_bi_static: device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(BIV_EHIP, "attn_decode_bi_static: hipGetSymbolAddress: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return BIV_OK;
+}
+
+}  // namespace biv
+
+extern "C" biv_status attn_decode_bi_static(const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
+                                            const int32_t* block_table, const int32_t* ctx, const int32_t* q_off,
+                                            void* out, int R, int q_len, int Hq, int Hkv, int D, int max_blocks,
+                                            int num_blocks, float scale, biv_dtype dt, biv_stream stream) {
+  using namespace biv;
+  BIV_REQUIRE(valid_dt(dt), "attn_decode_bi_static: bad dtype");
+  biv_status st = check_attn("attn_decode_bi_static", q, q_stride, k_cache, v_cache, block_table, ctx, out, R, q_len,
+                             Hq, Hkv, D, max_blocks, num_blocks);
+  if (st != BIV_OK) return st;
+  if (R == 0) return BIV_OK;
+  if (dt != BIV_BF16)  // the fp32 path uses no workspace
+    return attn_decode_bi(q, q_stride, k_cache, v_cache, block_table, ctx, q_off, out, R, q_len, Hq, Hkv, D,
+                          max_blocks, num_blocks, scale, dt, nullptr, 0, stream);
+  if (D != kHD) return fail(BIV_EUNSUPPORTED, "attn_decode_bi_static: bf16 path supports D == 128 only (D=%d)", D);
+  if (32 % (Hq / Hkv) != 0)
+    return fail(BIV_EUNSUPPORTED, "attn_decode_bi_static: bf16 path needs Hq/Hkv dividing 32 (got %d)", Hq / Hkv);
+  const size_t need = biv_attn_workspace_bytes_q(R, q_len, Hq, Hkv, max_blocks, BIV_ATTN_SEG_TOKENS);
+  BIV_REQUIRE(need > 0 && need <= (size_t)BIV_ATTN_STATIC_SCRATCH_BYTES,
+              "attn_decode_bi_static: this call needs %zu bytes of workspace, more than the library's %zu-byte "
+              "static scratch; use attn_decode_bi with a workspace", need, (size_t)BIV_ATTN_STATIC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  st = static_scratch(&ws);
+  if (st != BIV_OK) return st;
+  return launch_attn_bf16("attn_decode_bi_static", q, q_stride, k_cache, v_cache, block_table, ctx, q_off, out, R,
+                          q_len, Hq, Hkv, max_blocks, num_blocks, scale, BIV_ATTN_SEG_TOKENS, true, ws,
+                          (size_t)BIV_ATTN_STATIC_SCRATCH_BYTES, static_cast<hipStream_t>(stream));
+}
