@@ -8,11 +8,13 @@ pages, then Gumbel-max verification of the candidates (the KV overwrite of the
 fast-path slots runs inside every layer).  Inputs are resident in HBM before
 the timed region.
 
-Prints ONE JSON line: verified tokens/s, the slowdown of the invariant pass
-against the same pass with split-K GEMMs and load-adaptive attention splits,
-the attention kernel's roofline (HBM-bound; bytes = one read of each visible
-K/V row, timed with HIP events on the stream it runs on), and the CPU oracle
-timed on a bounded sample.
+Prints ONE JSON line: verified tokens/s; the slowdown of the invariant pass
+against the same pass with split-K GEMMs and load-adaptive attention splits
+(each shape's split chosen by timing the candidates); the attention kernel's
+roofline (the dominant kernel: HBM-bound, bytes = one read of each visible
+K/V row, timed with HIP events on the stream it runs on); the roofline of
+every kernel class of the step (each class's calls replayed as a HIP graph)
+and of the whole step; and the CPU oracle timed on a bounded sample.
 
     python bench.py [--steps 10] [--warmup 3] [--gpus 1] [--no-cpu-baseline]
 """
@@ -252,11 +254,14 @@ def gemm_only(args):
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 
 
-class KernelTimers:
-    """HIP event pairs around every call of the library's entry points during
-    eager passes, grouped by kernel class, on the stream the library launches
-    on (torch's current stream).  Installed by swapping the binding's module
-    functions (the pass looks them up at call time); removed afterwards."""
+class KernelCalls:
+    """Records every call of the library's entry points during one eager pass,
+    grouped by kernel class (installed by swapping the binding's module
+    functions, which the pass looks up at call time; removed afterwards).
+    ``time_classes`` then captures each class's calls, in pass order, as one
+    HIP graph and times its replays with HIP events on the capturing stream:
+    kernel time back to back, without the host's launch gaps that event pairs
+    around short eager calls would include."""
 
     NAMES = ("embed_rows", "rmsnorm_bi", "gemm_bi", "rope_kv_overwrite", "attn_decode_bi",
              "lm_head_gumbel_verify")
@@ -265,7 +270,7 @@ class KernelTimers:
         import invariant_verify_verifier_amd._lib as L
 
         self.torch, self.L = torch, L
-        self.pairs = {}
+        self.calls = {}
         self.orig = {n: getattr(L, n) for n in self.NAMES}
 
     @staticmethod
@@ -277,18 +282,12 @@ class KernelTimers:
         return (name,)
 
     def __enter__(self):
-        torch = self.torch
         for n in self.NAMES:
             fn = self.orig[n]
 
             def run(*a, _n=n, _fn=fn, **k):
-                s = torch.cuda.Event(enable_timing=True)
-                e = torch.cuda.Event(enable_timing=True)
-                s.record()
-                r = _fn(*a, **k)
-                e.record()
-                self.pairs.setdefault(self.key(_n, a, k), []).append((s, e))
-                return r
+                self.calls.setdefault(self.key(_n, a, k), []).append((_fn, a, k))
+                return _fn(*a, **k)
 
             setattr(self.L, n, run)
         return self
@@ -297,9 +296,31 @@ class KernelTimers:
         for n, fn in self.orig.items():
             setattr(self.L, n, fn)
 
-    def mean_ms(self):
-        self.torch.cuda.synchronize()
-        return {k: (float(np.mean([s.elapsed_time(e) for s, e in v])), len(v)) for k, v in self.pairs.items()}
+    def time_classes(self, reps=3):
+        """{class: (mean ms per call, calls per pass)}."""
+        n_calls = {key: len(lst) for key, lst in self.calls.items()}
+        torch = self.torch
+        out = {}
+        for key, lst in self.calls.items():
+            # a class with few calls per step is repeated so that the graph's
+            # own launch cost is spread over at least 32 kernels
+            lst = lst * max(1, -(-32 // len(lst)))
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for fn, a, k in lst:
+                    fn(*a, **k)
+            graph.replay()
+            torch.cuda.synchronize()
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(reps):
+                graph.replay()
+            e.record()
+            torch.cuda.synchronize()
+            out[key] = (s.elapsed_time(e) / (reps * len(lst)), n_calls[key])
+            del graph
+        return out
 
 
 def kernel_rooflines(sh, W, ctx, timers, steps):
@@ -1031,11 +1052,13 @@ def main():
     timer.on = True
     ms_eager = time_passes(torch, model, batch, caches, args.steps, attn_fn=attn, fused_head=True)
     timer.on = False
-    # eager passes with HIP events around every call of every kernel class
-    # (per-kernel rooflines and the whole step's)
-    with KernelTimers(torch) as kt:
-        time_passes(torch, model, batch, caches, args.steps, fused_head=True)
-    per_kernel, roof_ms_step = kernel_rooflines(env["sh"], N_REQ * K_CAND, ctx, kt.mean_ms(), args.steps)
+    # every call of one eager pass recorded by kernel class, each class then
+    # replayed as a graph of its own calls (per-kernel rooflines and the
+    # whole step's)
+    with KernelCalls(torch) as kc:
+        model.verify(batch, caches, fused_head=True)
+    torch.cuda.synchronize()
+    per_kernel, roof_ms_step = kernel_rooflines(env["sh"], N_REQ * K_CAND, ctx, kc.time_classes(), 1)
     # the timed step: the whole pass replayed as one HIP graph
     graph = model.capture(batch, caches, fused_head=True)
     for _ in range(args.warmup):
