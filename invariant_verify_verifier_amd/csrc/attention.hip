@@ -48,6 +48,7 @@ constexpr int kChunk = BIV_ATTN_CHUNK_TOKENS;
 constexpr int kSubsPerChunk = kChunk / kSub;
 constexpr int kSlot = kSub * kHD * 2;    // 8 KiB: K or V of one sub-tile
 constexpr int kRing = 5;                 // LDS slots per wave (40 KiB: four waves fill a CU's 160 KiB)
+static_assert(kRing == 5, "wait_ring: a full ring leaves four loads (32 copies) in flight");
 constexpr int kPagesPerWin = 64;         // page ids held in one register (lane i: page i of the window)
 constexpr int kPreWin = 4;               // page windows loaded at a wave's start (4096 tokens)
 constexpr float kLog2e = 1.4426950408889634f;
@@ -106,6 +107,26 @@ __device__ __forceinline__ void store_partial(float* po, float* pml, int64_t slo
   pml[slot * 128 + lane * 2 + 1] = l;
 }
 
+// One gfx950 global_load_lds_dwordx4 with the constant byte offset OFF:
+// lane i copies 16 bytes from sbase + voff_i + OFF to LDS bytes
+// m0v + OFF + 16i .. +15 (the instruction's offset field moves the global
+// address and the LDS address alike).  sbase (64-bit) and m0v are
+// wave-uniform; m0v is an LDS byte address.  Issued as inline asm so that
+// the compiler does not model the LDS write (it would wait for every
+// outstanding copy before any LDS read); the kernel orders the copies with
+// explicit vmcnt waits.  The asm sets M0 itself; the bf16 kernel has no
+// other reader of M0 (the compiler sets M0 immediately before each
+// instruction of its own that reads it).
+template <int OFF>
+__device__ __forceinline__ void lds_copy16(uint64_t sbase, unsigned voff, unsigned m0v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((unsigned)sbase);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((unsigned)(sbase >> 32));
+  const uint64_t sb = (uint64_t)lo | ((uint64_t)hi << 32);
+  const unsigned m0s = __builtin_amdgcn_readfirstlane(m0v);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3" ::"v"(voff), "s"(sb), "s"(m0s),
+               "i"(OFF) : "memory");
+}
+
 // Wait until at most 8n direct-to-LDS copies (n loads) are outstanding.
 __device__ __forceinline__ void wait_loads_after(int n) {
   switch (n) {
@@ -115,6 +136,26 @@ __device__ __forceinline__ void wait_loads_after(int n) {
     case 3: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
     default: asm volatile("s_waitcnt vmcnt(32)" ::: "memory"); break;
   }
+}
+
+// The same, with the common case (a full ring: n >= 4) as one wait.
+__device__ __forceinline__ void wait_ring(int n) {
+  if (n >= 4)
+    asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+  else
+    wait_loads_after(n);
+}
+
+// fp32 value of lane l ^ 32 combined with lane l's own: permlane32 swap
+// exchanges the two 32-lane halves of a copy of x, so for every lane the two
+// results are {x[l], x[l ^ 32]} in some order.
+__device__ __forceinline__ float max_with_other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_with_other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __fadd_rn(__uint_as_float(r[0]), __uint_as_float(r[1]));  // x[l] + x[l ^ 32]: fp32 add commutes
 }
 
 // (M, L, O) <- fold((M, L, O), (m, l, o)) over N outputs.  The products
@@ -254,6 +295,14 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
   // window, i.e. row 4c + i/16, position i%16, so it fetches piece
   // (i%16) ^ kv_swz(row) of that key.  kv_swz(4c + i/16) = 4(i/16) + c%4.
   const unsigned voff0 = 256u * (lane >> 4) + 16u * ((lane & 15) ^ (4 * (lane >> 4)));
+  // copy c of a page (keys 4c .. 4c+3) reads piece (i%16) ^ kv_swz(4c + i/16):
+  // the lane offset voff0 ^ 16c, and 1024c bytes into the page (the
+  // instruction's offset field)
+  const unsigned voff1 = voff0 ^ 16u, voff2 = voff0 ^ 32u, voff3 = voff0 ^ 48u;
+  // LDS byte address of the ring (wave-uniform), once
+  const unsigned ring_lds =
+      __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)ring);
+  const uint64_t page_bytes = (uint64_t)Hkv * 16 * kHD * 2, head_bytes = (uint64_t)kvh * 16 * kHD * 2;
   // the window holding load j's pages (its register is passed by value to
   // the copy: selecting between captured variables inside the lambda would
   // force them into private memory)
@@ -273,14 +322,19 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
       const int sh = 2 * (s & 15);
       valid_q = (valid_q & ~(3u << sh)) | ((uint32_t)(p0 >= 0) << sh) | ((uint32_t)(p1 >= 0) << (sh + 1));
     }
-    const uint16_t* cache = (j & 1) ? v_cache : k_cache;
-    const unsigned char* b0 =
-        reinterpret_cast<const unsigned char*>(cache + ((int64_t)(p0 >= 0 ? p0 : 0) * Hkv + kvh) * 16 * kHD);
-    const unsigned char* b1 =
-        reinterpret_cast<const unsigned char*>(cache + ((int64_t)(p1 >= 0 ? p1 : 0) * Hkv + kvh) * 16 * kHD);
-    unsigned char* dst = ring + slot * kSlot;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) lds_dma16((i < 4 ? b0 : b1) + 1024 * (i & 3), voff0 ^ (16u * (i & 3)), dst + 1024 * i);
+    const uint64_t cache = reinterpret_cast<uint64_t>((j & 1) ? v_cache : k_cache) + head_bytes;
+    const uint64_t b0 = cache + (uint64_t)(p0 >= 0 ? p0 : 0) * page_bytes;  // keys 0..15 of the sub-tile
+    const uint64_t b1 = cache + (uint64_t)(p1 >= 0 ? p1 : 0) * page_bytes;  // keys 16..31
+    const unsigned dst = ring_lds + (unsigned)(slot * kSlot);
+    // copy c of a page lands 1024c bytes into the page's half of the slot
+    lds_copy16<0>(b0, voff0, dst);
+    lds_copy16<1024>(b0, voff1, dst);
+    lds_copy16<2048>(b0, voff2, dst);
+    lds_copy16<3072>(b0, voff3, dst);
+    lds_copy16<0>(b1, voff0, dst + 4096);
+    lds_copy16<1024>(b1, voff1, dst + 4096);
+    lds_copy16<2048>(b1, voff2, dst + 4096);
+    lds_copy16<3072>(b1, voff3, dst + 4096);
   };
 
   // K read of step t: piece 2t + g of key li at position (2t + g) ^ kv_swz(li)
@@ -331,7 +385,7 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
     const uint32_t vb = valid_q >> (2 * (s & 15));
     const bool ok0 = vb & 1u, ok1 = vb & 2u;
     // ---- S^T = K Q^T
-    wait_loads_after(min(kRing - 1, total - 1 - 2 * s));
+    wait_ring(total - 1 - 2 * s);
     const unsigned char* Ks = ring + sk * kSlot;
     f32x16 sacc;
 #pragma unroll
@@ -365,7 +419,7 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
     float tmax = -INFINITY;
 #pragma unroll
     for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, x[v]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    tmax = max_with_other_half(tmax);
     // The row's reference max moves only when a score exceeds it by more
     // than kLazy (log2 units), so p <= 2^kLazy and the accumulators are
     // rescaled rarely; the result is the same softmax, and the decision
@@ -388,11 +442,11 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
         pb[v >> 3][v & 7] = (__bf16)p;
       }
     }
-    lsum = __fadd_rn(lsum, __shfl_xor(lsum, 32, 64));
+    lsum = sum_with_other_half(lsum);
     lc = __fadd_rn(__fmul_rn(lc, alpha), lsum);
     mc = mn;
     // ---- O^T += V^T P^T
-    wait_loads_after(min(kRing - 1, total - 2 - 2 * s));
+    wait_ring(total - 2 - 2 * s);
     unsigned char* Vs = ring + sv * kSlot;
     if (!(ok0 && ok1 && sub_base + kSub <= n_tok)) {  // wave-uniform: zero V rows of masked keys
       const u32x4 zero = {0u, 0u, 0u, 0u};
