@@ -107,24 +107,50 @@ __device__ __forceinline__ void store_partial(float* po, float* pml, int64_t slo
   pml[slot * 128 + lane * 2 + 1] = l;
 }
 
-// One gfx950 global_load_lds_dwordx4 with the constant byte offset OFF:
-// lane i copies 16 bytes from sbase + voff_i + OFF to LDS bytes
-// m0v + OFF + 16i .. +15 (the instruction's offset field moves the global
-// address and the LDS address alike).  sbase (64-bit) and m0v are
-// wave-uniform; m0v is an LDS byte address.  Issued as inline asm so that
-// the compiler does not model the LDS write (it would wait for every
-// outstanding copy before any LDS read); the kernel orders the copies with
-// explicit vmcnt waits.  The asm sets M0 itself; the bf16 kernel has no
-// other reader of M0 (the compiler sets M0 immediately before each
-// instruction of its own that reads it).
-template <int OFF>
-__device__ __forceinline__ void lds_copy16(uint64_t sbase, unsigned voff, unsigned m0v) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((unsigned)sbase);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((unsigned)(sbase >> 32));
-  const uint64_t sb = (uint64_t)lo | ((uint64_t)hi << 32);
-  const unsigned m0s = __builtin_amdgcn_readfirstlane(m0v);
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3" ::"v"(voff), "s"(sb), "s"(m0s),
-               "i"(OFF) : "memory");
+// A wave-uniform 64-bit value in SGPRs.  readfirstlane returns int: each
+// half goes through uint32_t so that the low half is zero-extended, not
+// sign-extended, when the two are put together.
+__device__ __forceinline__ uint64_t wave_uniform_u64(uint64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((unsigned)x);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((unsigned)(x >> 32));
+  return (uint64_t)lo | ((uint64_t)hi << 32);
+}
+
+// One ring slot's copies: two 16-token pages (K or V of one KV head) of
+// 4 KiB each, eight gfx950 global_load_lds_dwordx4.  Lane i of copy c of
+// page q reads 16 bytes at base_q + voff_c(i) + 1024c and writes them to LDS
+// bytes m0_q + 1024c + 16i .. +15: the instruction's offset field moves the
+// global address and the LDS address alike, so one M0 serves a page.
+// base_q (64-bit) and m0_q are wave-uniform; m0_q is an LDS byte address.
+// Issued as inline asm so that the compiler does not model the LDS writes
+// (it would wait for every outstanding copy before any LDS read); the
+// kernel orders the copies with explicit vmcnt waits.  The compiler cannot
+// see into the block, so it carries its own wait states: 5 before the first
+// load (an SGPR operand last written by a VALU instruction, such as
+// readfirstlane, needs 5 before a memory instruction reads it; an M0 write
+// needs 1 before an LDS DMA) and 1 after the second M0 write.  The bf16
+// kernel has no other reader of M0 (the compiler sets M0 immediately before
+// each instruction of its own that reads it).
+__device__ __forceinline__ void lds_copy_slot(uint64_t base0, uint64_t base1, unsigned m00, unsigned m01,
+                                              unsigned voff0, unsigned voff1, unsigned voff2, unsigned voff3) {
+  const uint64_t b0 = wave_uniform_u64(base0), b1 = wave_uniform_u64(base1);
+  const unsigned m0a = (uint32_t)__builtin_amdgcn_readfirstlane(m00);
+  const unsigned m0b = (uint32_t)__builtin_amdgcn_readfirstlane(m01);
+  asm volatile(
+      "s_mov_b32 m0, %6\n\t"
+      "s_nop 4\n\t"
+      "global_load_lds_dwordx4 %0, %4 offset:0\n\t"
+      "global_load_lds_dwordx4 %1, %4 offset:1024\n\t"
+      "global_load_lds_dwordx4 %2, %4 offset:2048\n\t"
+      "global_load_lds_dwordx4 %3, %4 offset:3072\n\t"
+      "s_mov_b32 m0, %7\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %5 offset:0\n\t"
+      "global_load_lds_dwordx4 %1, %5 offset:1024\n\t"
+      "global_load_lds_dwordx4 %2, %5 offset:2048\n\t"
+      "global_load_lds_dwordx4 %3, %5 offset:3072" ::"v"(voff0),
+      "v"(voff1), "v"(voff2), "v"(voff3), "s"(b0), "s"(b1), "s"(m0a), "s"(m0b)
+      : "memory");
 }
 
 // Wait until at most 8n direct-to-LDS copies (n loads) are outstanding.
@@ -326,15 +352,7 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
     const uint64_t b0 = cache + (uint64_t)(p0 >= 0 ? p0 : 0) * page_bytes;  // keys 0..15 of the sub-tile
     const uint64_t b1 = cache + (uint64_t)(p1 >= 0 ? p1 : 0) * page_bytes;  // keys 16..31
     const unsigned dst = ring_lds + (unsigned)(slot * kSlot);
-    // copy c of a page lands 1024c bytes into the page's half of the slot
-    lds_copy16<0>(b0, voff0, dst);
-    lds_copy16<1024>(b0, voff1, dst);
-    lds_copy16<2048>(b0, voff2, dst);
-    lds_copy16<3072>(b0, voff3, dst);
-    lds_copy16<0>(b1, voff0, dst + 4096);
-    lds_copy16<1024>(b1, voff1, dst + 4096);
-    lds_copy16<2048>(b1, voff2, dst + 4096);
-    lds_copy16<3072>(b1, voff3, dst + 4096);
+    lds_copy_slot(b0, b1, dst, dst + 4096, voff0, voff1, voff2, voff3);  // pages to the slot's two halves
   };
 
   // K read of step t: piece 2t + g of key li at position (2t + g) ^ kv_swz(li)
