@@ -94,6 +94,10 @@ __device__ __forceinline__ float wave_max(float v) {
 // the copies with explicit vmcnt waits; loads the compiler issues itself stay
 // correct, since untracked copies only make its vmcnt waits stricter.  M0
 // (the LDS base of the copy) is not used by anything else in these kernels.
+// kStream: the copy carries the non-temporal hint, so that a stream read
+// once (a weight) does not displace data that is read again (activations
+// shared by every column block) from the L2.  Only cache placement changes.
+template <bool kStream = false>
 __device__ __forceinline__ void lds_dma16(const void* sbase, unsigned voff, void* dst) {
   const unsigned m0v =
       __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)dst);
@@ -102,7 +106,10 @@ __device__ __forceinline__ void lds_dma16(const void* sbase, unsigned voff, void
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)sbase);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((unsigned)((uintptr_t)sbase >> 32));
   const uint64_t sb = (uint64_t)lo | ((uint64_t)hi << 32);
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb), "s"(m0v) : "memory");
+  if constexpr (kStream)
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sb), "s"(m0v) : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb), "s"(m0v) : "memory");
 }
 
 __device__ __forceinline__ void vm_wait0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

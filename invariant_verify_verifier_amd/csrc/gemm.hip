@@ -256,11 +256,23 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_dma_kernel(const 
     gbase[q] = reinterpret_cast<const unsigned char*>(src + (int64_t)first * K + k_begin);
     voff[q] = (unsigned)((row - first) * K * 2 + c_log * 16);
   }
+  // Window q of every wave is an A window for q < A_PER_WAVE, a B window
+  // after.  The weight (B) is streamed with the non-temporal hint in the
+  // tiles where that measured faster -- rows per tile <= 64 (3-9% at M = 64)
+  // and the 256-column tiles (lm_head 2.5% at M = 512) -- which keeps the
+  // activation rows that every column block re-reads in the L2.
+  constexpr int A_PER_WAVE = (BM / RPW) / NW;
+  static_assert((BM / RPW) % NW == 0, "A windows must split evenly over the waves");
+  constexpr bool kStreamB = BM <= 64 || BN >= 256;
   auto issue = [&](int kt) {
     unsigned char* slot = smem + (kt % STAGES) * STAGE;
 #pragma unroll
-    for (int q = 0; q < PER_WAVE; ++q)
-      lds_dma16(gbase[q] + (int64_t)kt * ROW, voff[q], slot + (wave + NW * q) * 1024);
+    for (int q = 0; q < PER_WAVE; ++q) {
+      if (q < A_PER_WAVE)
+        lds_dma16(gbase[q] + (int64_t)kt * ROW, voff[q], slot + (wave + NW * q) * 1024);
+      else
+        lds_dma16<kStreamB>(gbase[q] + (int64_t)kt * ROW, voff[q], slot + (wave + NW * q) * 1024);
+    }
   };
 
   // fragment offsets: row li of a 32-row block, logical chunk 2 ks + g
