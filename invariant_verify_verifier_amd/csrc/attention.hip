@@ -90,9 +90,13 @@ struct AttnWs {
 // Partial (m, l, o[64]) of a lane -> slot `slot` of (po, pml): sixteen 1 KiB
 // stores of four values each (streaming stores for segment partials; chunk
 // partials, few and read back soon, go through the caches), then m and l.
+// Lanes of rows past the row block's last (live false) store nothing: the
+// combine never reads them, and at one query position per request only 4 of
+// the 32 rows are real.
 template <bool kStream>
-__device__ __forceinline__ void store_partial(float* po, float* pml, int64_t slot, int lane, float m, float l,
-                                              const float* o) {
+__device__ __forceinline__ void store_partial(float* po, float* pml, int64_t slot, int lane, bool live, float m,
+                                              float l, const float* o) {
+  if (!live) return;
   float* so = po + slot * 4096;
 #pragma unroll
   for (int qg = 0; qg < 16; ++qg) {
@@ -518,7 +522,7 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
           fold_into<64>(Ms, Ls, Os, mc, lc, o);
         } else {
           const int64_t chunk = ((int64_t)v * Hkv + kvh) * nseg_max * (seg_tokens / kChunk) + sub_base / kChunk;
-          store_partial<false>(ws.chunk_o, ws.chunk_ml, chunk, lane, mc, lc, o);
+          store_partial<false>(ws.chunk_o, ws.chunk_ml, chunk, lane, row_ok, mc, lc, o);
         }
       } else {
         fold_into<64>(Ms, Ls, Os, mc, lc, o);
@@ -551,7 +555,8 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
   }
   // the segment result (or, for a split segment, the fold of its first
   // part's chunks) -> workspace; attn_combine_kernel folds on from there
-  store_partial<true>(ws.part_o, ws.part_ml, ((int64_t)v * Hkv + kvh) * nseg_max + seg, lane, Ms, Ls, Os);
+  store_partial<true>(ws.part_o, ws.part_ml, ((int64_t)v * Hkv + kvh) * nseg_max + seg, lane, row_ok, Ms, Ls,
+                      Os);
 }
 
 // Work list for large grids: every full segment first, then the partial last
@@ -675,15 +680,78 @@ static int resident_attn_waves() {
 // the first pass and its values 4q .. 4q+3, q = 4z + t / 64 (dims
 // 32(q/4) + 8(q%4) + 4g .. +3 of row (t%64) % 32).  Up to kCombBatch segment
 // partials, and kChunkBatch chunk partials, are loaded at once.
+//
+// When segments were split, attn_chunk_fold_kernel completes every split
+// segment first, all segments of a request in parallel (the chain of folds
+// is what bounds this pass at small batch), and the second pass then folds
+// segments only (chunks_folded).  The folds and their order are the same.
 constexpr int kCombZ = 4;  // workgroups per (KV head, row block)
-constexpr int kCombThreads = 1024 / kCombZ, kCombBatch = 8, kChunkBatch = 4;
+constexpr int kCombThreads = 1024 / kCombZ, kCombBatch = 8, kChunkBatch = 4, kChunkFoldBatch = 8;
+
+// A split segment's partial: the fold of its first part's chunks from the
+// first pass, then its later chunks folded on in ascending order; written to
+// the segment's first chunk slot, which the first pass leaves unused (the
+// first part folds its chunks in registers).  Grid (segment x KV head, row
+// block, kCombZ); threads as in the second pass.
+__global__ __launch_bounds__(kCombThreads) void attn_chunk_fold_kernel(const int32_t* __restrict__ ctx,
+                                                                       const int32_t* __restrict__ q_off, int q_len,
+                                                                       int Hq, int Hkv, int max_blocks, int seg_tokens,
+                                                                       int nseg_max, AttnWs ws, int blk_pos, int n_rb,
+                                                                       int parts) {
+  const int sg = (int)(blockIdx.x / (unsigned)Hkv), kvh = (int)blockIdx.x - sg * Hkv, v = blockIdx.y;
+  const int r = v / n_rb, j0 = (v - r * n_rb) * blk_pos;
+  const int tid = threadIdx.x, q = blockIdx.z * (kCombThreads / 64) + (tid >> 6), lane = tid & 63,
+            li = lane & 31;
+  const ReqRows rr = req_rows(q_off, r, q_len);
+  const int G = Hq / Hkv, jn = min(blk_pos, rr.n - j0), nrows = jn * G;
+  if (jn <= 0 || li >= nrows) return;
+  const int n_tok = min(ctx[r] + j0 + jn, max_blocks * 16);
+  const int nseg = (n_tok + seg_tokens - 1) / seg_tokens;
+  if (sg >= nseg) return;
+  const int part_tok = seg_tokens / parts, cps = seg_tokens / kChunk, cpp = part_tok / kChunk;
+  const int keys = min((sg + 1) * seg_tokens, n_tok) - sg * seg_tokens;
+  if (keys <= part_tok) return;  // not split: its partial is complete
+  const int nch = (keys + kChunk - 1) / kChunk;
+  const int64_t slot = ((int64_t)v * Hkv + kvh) * nseg_max + sg;
+  float o[4], m, l;
+  {
+    const f32x4 w = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ws.part_o + slot * 4096) + q * 64 + lane);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[c] = w[c];
+    m = ws.part_ml[slot * 128 + lane * 2 + 0];
+    l = ws.part_ml[slot * 128 + lane * 2 + 1];
+  }
+  for (int c0 = cpp; c0 < nch; c0 += kChunkFoldBatch) {
+    float co[kChunkFoldBatch][4], cm[kChunkFoldBatch], cl[kChunkFoldBatch];
+#pragma unroll
+    for (int e = 0; e < kChunkFoldBatch; ++e) {
+      if (c0 + e < nch) {
+        const int64_t cs = slot * cps + c0 + e;
+        const f32x4 w = *(reinterpret_cast<const f32x4*>(ws.chunk_o + cs * 4096) + q * 64 + lane);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) co[e][c] = w[c];
+        cm[e] = ws.chunk_ml[cs * 128 + lane * 2 + 0];
+        cl[e] = ws.chunk_ml[cs * 128 + lane * 2 + 1];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < kChunkFoldBatch; ++e)
+      if (c0 + e < nch) fold_into<4>(m, l, o, cm[e], cl[e], co[e]);
+  }
+  const int64_t cs0 = slot * cps;  // chunk 0 of the segment: never written by the first pass
+  *(reinterpret_cast<f32x4*>(ws.chunk_o + cs0 * 4096) + q * 64 + lane) = f32x4{o[0], o[1], o[2], o[3]};
+  if (q == 0) {  // (m, l) of a row are the same in every thread of its lane
+    ws.chunk_ml[cs0 * 128 + lane * 2 + 0] = m;
+    ws.chunk_ml[cs0 * 128 + lane * 2 + 1] = l;
+  }
+}
 
 __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(const int32_t* __restrict__ ctx,
                                                                     const int32_t* __restrict__ q_off,
                                                                     uint16_t* __restrict__ out, int q_len, int Hq,
                                                                     int Hkv, int max_blocks, int seg_tokens,
                                                                     int nseg_max, AttnWs ws, int blk_pos, int n_rb,
-                                                                    int parts) {
+                                                                    int parts, int chunks_folded) {
   const int kvh = blockIdx.x, v = blockIdx.y;  // v: row block, as in the first pass
   const int r = v / n_rb, j0 = (v - r * n_rb) * blk_pos;
   const int tid = threadIdx.x, q = blockIdx.z * (kCombThreads / 64) + (tid >> 6), lane = tid & 63, g = lane >> 5,
@@ -705,12 +773,16 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(const int32_
 #pragma unroll
     for (int b = 0; b < kCombBatch; ++b) {
       if (s0 + b < nseg) {
-        const int64_t sl = slot0 + s0 + b;
-        const f32x4 w = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ws.part_o + sl * 4096) + q * 64 + lane);
+        // a split segment completed by attn_chunk_fold_kernel sits in its first chunk slot
+        const bool done = chunks_folded && seg_keys(s0 + b) > part_tok;
+        const int64_t sl = done ? (slot0 + s0 + b) * cps : slot0 + s0 + b;
+        const float* po = done ? ws.chunk_o : ws.part_o;
+        const float* pml = done ? ws.chunk_ml : ws.part_ml;
+        const f32x4 w = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(po + sl * 4096) + q * 64 + lane);
 #pragma unroll
         for (int c = 0; c < 4; ++c) o[b][c] = w[c];
-        m[b] = ws.part_ml[sl * 128 + lane * 2 + 0];
-        l[b] = ws.part_ml[sl * 128 + lane * 2 + 1];
+        m[b] = pml[sl * 128 + lane * 2 + 0];
+        l[b] = pml[sl * 128 + lane * 2 + 1];
       }
     }
 #pragma unroll
@@ -718,7 +790,7 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(const int32_
       const int sg = s0 + b;
       if (sg >= nseg) continue;
       const int keys = seg_keys(sg);
-      if (keys > part_tok) {  // split: the segment's chunks after its first part, loaded kChunkBatch at a time
+      if (!chunks_folded && keys > part_tok) {  // split: the segment's chunks after its first part, kChunkBatch at a time
         const int nch = (keys + kChunk - 1) / kChunk;
         for (int c0 = cpp; c0 < nch; c0 += kChunkBatch) {
           float co[kChunkBatch][4], cm[kChunkBatch], cl[kChunkBatch];
@@ -912,8 +984,15 @@ static biv_status launch_attn_bf16(const char* who, const void* q, int64_t q_str
                        seg_tokens, nseg_max, ws, items, blk_pos, n_rb, 1, head_fastest ? 1 : 0);
   biv_status st = launched(who);
   if (st != BIV_OK || (nseg_max <= 1 && parts == 1)) return st;
+  if (parts > 1) {  // complete the split segments, every segment of a request at once
+    BIV_REQUIRE((int64_t)Hkv * nseg_max <= 0x7fffffff, "%s: too many segments", who);
+    hipLaunchKernelGGL(attn_chunk_fold_kernel, dim3((unsigned)(Hkv * nseg_max), Rv, kCombZ), dim3(kCombThreads), 0, s,
+                       ctx, q_off, q_len, Hq, Hkv, max_blocks, seg_tokens, nseg_max, ws, blk_pos, n_rb, parts);
+    st = launched(who);
+    if (st != BIV_OK) return st;
+  }
   hipLaunchKernelGGL(attn_combine_kernel, dim3(Hkv, Rv, kCombZ), dim3(kCombThreads), 0, s, ctx, q_off, static_cast<uint16_t*>(out),
-                     q_len, Hq, Hkv, max_blocks, seg_tokens, nseg_max, ws, blk_pos, n_rb, parts);
+                     q_len, Hq, Hkv, max_blocks, seg_tokens, nseg_max, ws, blk_pos, n_rb, parts, parts > 1 ? 1 : 0);
   return launched(who);
 }
 
