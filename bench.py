@@ -671,27 +671,36 @@ def micro_norm_gemm(torch, biv, iters):
         x = x_all[:M]
         h = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
         out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-        sp = biv.splitk_auto_splits(M, N, H)
-        wsk = torch.empty(max(biv.splitk_workspace_bytes(M, N, sp), 16), dtype=torch.uint8, device="cuda")
 
         def run_bi(i):
             biv.rmsnorm_bi(x, gamma, h, eps)
             biv.gemm_bi(h, ws[i % 4], out)
 
-        def run_sk(i):
-            biv.rmsnorm_bi(x, gamma, h, eps)
-            biv.gemm_splitk(h, ws[i % 4], out, sp, wsk)
+        def run_sk(sp, wsk):
+            def run(i):
+                biv.rmsnorm_bi(x, gamma, h, eps)
+                biv.gemm_splitk(h, ws[i % 4], out, sp, wsk)
+            return run
 
         t_bi, p90 = _event_times(torch, run_bi, iters)
-        t_sk, _ = _event_times(torch, run_sk, iters)
+        # the comparison: split-K timed at 1, 2, 4 and 8 splits of K, the fastest kept (1 split is gemm_bi)
+        t_by = {}
+        for sp in (1, 2, 4, 8):
+            wsk = torch.empty(max(biv.splitk_workspace_bytes(M, N, sp), 16), dtype=torch.uint8, device="cuda")
+            t_by[sp] = _event_times(torch, run_sk(sp, wsk), iters)[0]
+            del wsk
+        sp = min(t_by, key=t_by.get)
+        t_sk = t_by[sp]
         byts = N * H * 2 + M * H * 2 * 2 + M * N * 2
         flops = 2.0 * M * N * H
         t_roof = max(byts / (HBM_PEAK_GBS * 1e9), flops / (MFMA_PEAK_TFLOPS * 1e12)) * 1e3
         points.append({"M": M, "ms": round(t_bi, 5), "ms_p90": round(p90, 5),
                        "bound": "hbm" if byts / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_PEAK_TFLOPS * 1e12) else "mfma",
                        "roofline_ms": round(t_roof, 5), "frac": round(t_roof / t_bi, 4),
-                       "splitk_splits": sp, "splitk_ms": round(t_sk, 5), "slowdown_vs_splitk": round(t_bi / t_sk, 4)})
-        print(f"[micro] rmsnorm+gemm M={M}: {t_bi * 1e3:.1f} us (roof {t_roof * 1e3:.1f}), split-K x{sp} "
+                       "splitk_splits": sp, "splitk_ms": round(t_sk, 5), "slowdown_vs_splitk": round(t_bi / t_sk, 4),
+                       "splitk_ms_by_splits": {str(k): round(v, 5) for k, v in t_by.items()},
+                       "splitk_auto_splits": biv.splitk_auto_splits(M, N, H)})
+        print(f"[micro] rmsnorm+gemm M={M}: {t_bi * 1e3:.1f} us (roof {t_roof * 1e3:.1f}), split-K best x{sp} "
               f"{t_sk * 1e3:.1f} us", file=sys.stderr, flush=True)
     # oracle: the same two steps in fp64 on the host
     w64 = _f64_bf16(torch, ws[0])
@@ -734,21 +743,31 @@ def micro_attention(torch, biv, iters):
             bt, cx, q = bt_all[:B].contiguous(), cx_all[:B].contiguous(), q_all[:B * q_len]
             ob = o[:B * q_len]
             wsb = torch.empty(biv.attn_workspace_bytes(B, Hkv, lay.max_blocks), dtype=torch.uint8, device="cuda")
-            split = biv.attn_adaptive_split(B, Hkv, lay.max_blocks)
-            wsa = torch.empty(max(biv.attn_workspace_bytes(B, Hkv, lay.max_blocks, split), 16), dtype=torch.uint8,
-                              device="cuda")
             run_bi = lambda i: biv.attn_decode_bi(q, kc, vc, bt, cx, ob, q_len, scale, wsb)
-            run_ad = lambda i: biv.attn_decode_adaptive(q, kc, vc, bt, cx, ob, q_len, scale, wsa, split_tokens=split)
             t_bi, p90 = _event_times(torch, run_bi, iters, pre=flush.zero_)
-            t_ad, _ = _event_times(torch, run_ad, iters, pre=flush.zero_)
+            # the comparison: the load-adaptive split, half of it and twice it (multiples of 256 tokens
+            # within the block table's capacity), each timed, the fastest kept
+            auto = biv.attn_adaptive_split(B, Hkv, lay.max_blocks)
+            cap = -(-lay.max_blocks * 16 // 256) * 256
+            t_by = {}
+            for sp_tok in sorted({max(256, auto // 2 // 256 * 256), auto, min(cap, auto * 2)}):
+                wsa = torch.empty(max(biv.attn_workspace_bytes(B, Hkv, lay.max_blocks, sp_tok), 16),
+                                  dtype=torch.uint8, device="cuda")
+                run_ad = lambda i: biv.attn_decode_adaptive(q, kc, vc, bt, cx, ob, q_len, scale, wsa,
+                                                            split_tokens=sp_tok)
+                t_by[sp_tok] = _event_times(torch, run_ad, iters, pre=flush.zero_)[0]
+                del wsa
+            split = min(t_by, key=t_by.get)
+            t_ad = t_by[split]
             byts = float((ctx_all[:B].astype(np.int64) + q_len).sum()) * Hkv * D * 2 * 2
             t_roof = byts / (HBM_PEAK_GBS * 1e9) * 1e3
             points.append({"B": B, "ms": round(t_bi, 5), "ms_p90": round(p90, 5), "bytes": byts,
                            "GBps": round(byts / (t_bi * 1e-3) / 1e9, 1), "roofline_ms": round(t_roof, 5),
                            "frac": round(t_roof / t_bi, 4), "adaptive_split": split, "adaptive_ms": round(t_ad, 5),
-                           "slowdown_vs_adaptive": round(t_bi / t_ad, 4)})
+                           "slowdown_vs_adaptive": round(t_bi / t_ad, 4), "adaptive_auto_split": auto,
+                           "adaptive_ms_by_split": {str(k): round(v, 5) for k, v in t_by.items()}})
             print(f"[micro] attention q_len={q_len} B={B}: {t_bi * 1e3:.1f} us ({t_roof / t_bi:.2f} of HBM), "
-                  f"adaptive split {split}: {t_ad * 1e3:.1f} us", file=sys.stderr, flush=True)
+                  f"adaptive best split {split}: {t_ad * 1e3:.1f} us", file=sys.stderr, flush=True)
         out[f"q_len={q_len}"] = points
     # oracle: decode (q_len 1) at B = 1 and 16, on host copies of the pages used
     cpu = []
