@@ -171,7 +171,7 @@ biv_status gemm_bi(const void* A, const void* B, void* C, int64_t M, int64_t N, 
  * Two launches: the chunk/segment pass, then (only when some request spans
  * more than one segment, or segments are split) the fold of the partials;
  * large grids add a one-workgroup launch before them that orders the
- * segments.  Where the grid of segments would hold fewer than 512 waves
+ * segments.  Where the grid of segments would hold fewer than 1024 waves
  * (decided by R, Hkv and max_blocks alone), each segment is taken by
  * several waves over consecutive 256-token chunks: the first folds its
  * chunks, the later ones store their chunk partials, and the second launch

@@ -623,10 +623,10 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(const int32_t* __restri
 }
 
 // Parts per segment: halve the parts' length while the grid of segments
-// holds fewer than kSplitBelow potential waves (half a round of resident
-// waves on a 256-CU device), down to one 256-token chunk per part.  From the
-// call's shape alone.
-constexpr int64_t kSplitBelow = 512;
+// holds fewer than kSplitBelow potential waves (one round of resident waves
+// on a 256-CU device: a CU streams fastest with all four of its wave slots
+// busy), down to one 256-token chunk per part.  From the call's shape alone.
+constexpr int64_t kSplitBelow = 1024;
 static int attn_parts(int64_t Rv, int Hkv, int64_t nseg_max, int seg_tokens) {
   const int cps = seg_tokens / kChunk;
   const int64_t potential = Rv * Hkv * nseg_max;
@@ -943,15 +943,20 @@ static biv_status launch_attn_bf16(const char* who, const void* q, int64_t q_str
   const int Rv = R * n_rb;  // row blocks
   BIV_REQUIRE(aligned16(q) && aligned16(k_cache) && aligned16(v_cache) && q_stride % 8 == 0,
               "%s: q (and its row stride) and the caches must be 16-byte aligned", who);
-  const size_t need = biv_attn_workspace_bytes(Rv, Hkv, max_blocks, seg_tokens);
-  BIV_REQUIRE(workspace != nullptr && workspace_bytes >= need, "%s: workspace needs %zu bytes (got %zu)", who, need,
-              workspace_bytes);
-  BIV_REQUIRE(aligned16(workspace), "%s: workspace must be 16-byte aligned", who);
-  const int nseg_max = (int)cdiv((int64_t)max_blocks * 16, seg_tokens);
-  BIV_REQUIRE(nseg_max <= 0x7fffffff, "%s: too many segments", who);
+  BIV_REQUIRE(seg_tokens > 0 && seg_tokens % kChunk == 0, "%s: segment size %d is not a multiple of %d", who,
+              seg_tokens, kChunk);
+  const int64_t nseg_max64 = cdiv((int64_t)max_blocks * 16, seg_tokens);
+  BIV_REQUIRE(nseg_max64 <= 0x7fffffff, "%s: too many segments", who);
+  const int nseg_max = (int)nseg_max64;
   // Segments split over several waves where the grid would otherwise hold
   // few waves (decided by the call's shape alone; no bits change).
   const int parts = allow_split ? attn_parts(Rv, Hkv, nseg_max, seg_tokens) : 1;
+  // the layout this launch uses (biv_attn_workspace_bytes, which allows for
+  // splits, is never smaller)
+  const size_t need = attn_ws_floats(Rv, Hkv, nseg_max, seg_tokens, parts) * sizeof(float);
+  BIV_REQUIRE(workspace != nullptr && workspace_bytes >= need, "%s: workspace needs %zu bytes (got %zu)", who, need,
+              workspace_bytes);
+  BIV_REQUIRE(aligned16(workspace), "%s: workspace must be 16-byte aligned", who);
   const AttnWs ws = attn_ws_layout(workspace, Rv, Hkv, nseg_max, seg_tokens, parts);
   // A grid of at least four rounds of resident waves is launched in LPT
   // order from a work list (decided by the call's shape alone).

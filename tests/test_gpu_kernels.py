@@ -900,6 +900,27 @@ def test_attention_adaptive_matches_oracle(biv):
     check_bf16(f64(out), _attn_ref(lay, kc, vc, q, q_len), "attention adaptive")
 
 
+
+def test_attention_adaptive_any_split_fits_smallest_split_workspace(biv):
+    """The load-adaptive call never splits a segment over waves, so a
+    workspace sized for its smallest segment (256 tokens: the most segment
+    partials) serves every larger one -- what a comparison pass that times
+    several splits with one workspace relies on; each split still matches
+    the oracle."""
+    q_len = 8
+    ctx = [600, 4000, 9000]  # few requests: the invariant call would split these segments
+    lay, kc, vc, q = _attn_inputs(len(ctx), q_len, 32, 8, 128, ctx, seed=91)
+    ws = torch.empty(biv.attn_workspace_bytes(len(ctx), 8, lay.max_blocks, 256), dtype=torch.uint8, device=DEV)
+    ref = _attn_ref(lay, kc, vc, q, q_len)
+    qd, kcd, vcd = dev_bf16(q), dev_bf16(kc), dev_bf16(vc)
+    bt, cx = dev_i32(lay.block_table), dev_i32(lay.ctx)
+    for split in (256, 512, 1024, 2048, 4096, 8192):
+        announce("attention adaptive, one workspace, split", split)
+        out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+        biv.attn_decode_adaptive(qd, kcd, vcd, bt, cx, out, q_len, 1.0 / math.sqrt(128), ws, split_tokens=split)
+        sync()
+        check_bf16(f64(out), ref, f"attention adaptive split {split}")
+
 # =====================================================================
 # split-K, RoPE, SwiGLU, embedding
 # =====================================================================
