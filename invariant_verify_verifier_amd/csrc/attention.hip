@@ -24,12 +24,13 @@
 // sub-tile by sub-tile in ascending order; each finished chunk's partial
 // (m, l, o) is left-folded into the segment result in registers (in the
 // later parts of a split segment it is stored instead).  Segment results
-// (and stored chunk partials) go to the workspace; a second, small kernel
-// completes split segments' folds, left-folds the segments in ascending
-// order and writes the output (a request with a single, unsplit segment is
-// written directly).  A kernel boundary, not a device-wide fence, makes the
-// partials visible: on gfx950 such a fence writes back and invalidates the
-// whole L2 of an XCD.
+// (and stored chunk partials) go to the workspace; where segments were
+// split, a small kernel completes each split segment's fold (all segments
+// of a request at once), and a second small kernel left-folds the segments
+// in ascending order and writes the output (a request with a single,
+// unsplit segment is written directly).  Kernel boundaries, not device-wide
+// fences, make the partials visible: on gfx950 such a fence writes back and
+// invalidates the whole L2 of an XCD.
 //
 // Every boundary is an absolute position and every fold runs in ascending
 // order, so a row's bits depend only on its own query, its own request's KV
