@@ -793,6 +793,38 @@ def test_attention_bf16_batch_invariance(biv):
         assert np.array_equal(out2[slot * q_len:(slot + 1) * q_len], alone), f"trial {trial}"
 
 
+
+@pytest.mark.parametrize("q_len", [1, 8])
+def test_attention_split_segments_equal_unsplit(biv, q_len):
+    """A request alone is few segment waves, so each segment is split over
+    16 waves (later parts store per-chunk partials, completed by the chunk
+    fold before the segment fold); beside 63 other requests the grid holds
+    at least 1024 waves and nothing is split.  Its rows are the same bits
+    either way, across a split single segment, a part left without keys, a
+    ragged last chunk and exact segment boundaries."""
+    Hq, Hkv, D = 32, 8, 128
+    for L in (300, 4096 - q_len, 4097 - q_len, 5000, 9000, 12290):
+        lay, kc, vc, q = _attn_inputs(1, q_len, Hq, Hkv, D, [L], seed=95)
+        announce("attention split vs unsplit, alone", q_len, L)
+        alone = bits(_run_attn(biv, lay, kc, vc, q, q_len))
+        slot, R = 7, 64
+        ctx = [100] * R
+        ctx[slot], ctx[11] = L, 4200  # one filler past 4096 keys: at least two segments per request
+        lay2 = wl.paged_layout(ctx, q_len, seed=96, spare_blocks=2)
+        assert R * Hkv * -(-lay2.max_blocks * 16 // biv.ATTN_SEG_TOKENS) >= 1024  # unsplit grid
+        kc2 = wl.normal_bf16(97, (lay2.num_blocks, Hkv, 16, D))
+        vc2 = wl.normal_bf16(98, (lay2.num_blocks, Hkv, 16, D))
+        q2 = wl.normal_bf16(99, (R * q_len, Hq, D))
+        for b in range(lay.max_blocks):
+            src, dst = lay.block_table[0, b], lay2.block_table[slot, b]
+            if src >= 0:
+                kc2[dst] = kc[src]
+                vc2[dst] = vc[src]
+        q2[slot * q_len:(slot + 1) * q_len] = q
+        announce("attention split vs unsplit, batched", q_len, L)
+        out2 = bits(_run_attn(biv, lay2, kc2, vc2, q2, q_len))
+        assert np.array_equal(out2[slot * q_len:(slot + 1) * q_len], alone), (q_len, L)
+
 def test_attention_bf16_verify_rows_equal_single_decodes(biv):
     """Row j of a K=8 verify block equals, bit for bit, the same query decoded
     alone (K=1) at context L+j: extra masked keys and chunks fold as no-ops."""
