@@ -168,15 +168,15 @@ biv_status gemm_bi(const void* A, const void* B, void* C, int64_t M, int64_t N, 
  * ascending order.  Every split point is a fixed absolute position, so a
  * row's result depends only on its own request's data and length.
  * Positions >= ctx[r] + q_len_r read as empty (values zero, keys masked).
- * Two launches: the chunk/segment pass, then (only when some request spans
+ * Launches: the chunk/segment pass, then (only when some request spans
  * more than one segment, or segments are split) the fold of the partials;
  * large grids add a one-workgroup launch before them that orders the
  * segments.  Where the grid of segments would hold fewer than 1024 waves
  * (decided by R, Hkv and max_blocks alone), each segment is taken by
  * several waves over consecutive 256-token chunks: the first folds its
- * chunks, the later ones store their chunk partials, and the second launch
- * folds those on in the same ascending order -- the same fold, so the same
- * bits.  The fp32 path folds all chunk partials of a row in one ascending
+ * chunks, the later ones store their chunk partials, and a launch between
+ * the two folds those on in the same ascending order, every segment of a
+ * request at once -- the same fold, so the same bits.  The fp32 path folds all chunk partials of a row in one ascending
  * left fold (one launch).
  *
  * Supported: dt BIV_BF16 with D == 128 and Hq/Hkv dividing 32 (bf16 MFMA
