@@ -227,8 +227,8 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
     int seg_tokens, int nseg_max, AttnWs ws, const int32_t* __restrict__ items, int blk_pos, int n_rb, int parts,
     int head_fastest) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kRing * kSlot];
-  // grid: (segment part, KV head, row block); (KV head, segment, row block)
-  // when head_fastest (no splits, no work list); or with a work list (parts
+  // grid: (segment part, KV head, row block); (KV head, segment part, row
+  // block) when head_fastest (no work list); or with a work list (parts
   // == 1) a 1-D grid of (list entry, KV head), KV head fastest; an entry is
   // v * nseg_max + seg.  Row block v = r * n_rb + b holds query positions
   // b*blk_pos .. +blk_pos-1 of request r (one block, v = r, whenever
@@ -246,18 +246,15 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
     v = e / nseg_max;
     seg = e - v * nseg_max;
   } else {
+    const unsigned sx = head_fastest ? blockIdx.y : blockIdx.x;  // the segment (and part)
     if constexpr (kParts) {
-      seg = (int)(blockIdx.x / (unsigned)parts);
-      part = (int)blockIdx.x - seg * parts;
+      seg = (int)(sx / (unsigned)parts);
+      part = (int)sx - seg * parts;
     } else {
-      seg = blockIdx.x;
+      seg = (int)sx;
     }
-    kvh = blockIdx.y;
+    kvh = head_fastest ? blockIdx.x : blockIdx.y;
     v = blockIdx.z;
-    if (!kParts && head_fastest) {
-      kvh = blockIdx.x;
-      seg = blockIdx.y;
-    }
   }
   const int part_tok = kParts ? seg_tokens / parts : seg_tokens;
   const int tok_begin = seg * seg_tokens + part * part_tok;  // a multiple of kChunk
@@ -972,20 +969,21 @@ static biv_status launch_attn_bf16(const char* who, const void* q, int64_t q_str
     if (st != BIV_OK) return st;
     grid = dim3((unsigned)waves);
   }
-  // Without splits or a list, calls whose requests may span four or more
-  // segments launch the KV heads of a segment together (decided by the
+  // Without a list, calls whose requests may span four or more segments
+  // launch the KV heads of a segment (part) together, so the eight waves
+  // reading adjacent pieces of the same pages run at once (decided by the
   // call's shape alone): 5-7% faster for 16 and 32 requests of
   // U[512, 32768], while the 8B pass's contexts (at most three segments)
   // run 0.8% faster segment first.
-  const bool head_fastest = parts == 1 && items == nullptr && nseg_max >= 4 && nseg_max <= 65535;
-  if (head_fastest) grid = dim3((unsigned)Hkv, (unsigned)nseg_max, (unsigned)Rv);
+  const bool head_fastest = items == nullptr && nseg_max >= 4 && nseg_max * parts <= 65535;
+  if (head_fastest) grid = dim3((unsigned)Hkv, (unsigned)(nseg_max * parts), (unsigned)Rv);
   // segments split over waves take the kernel with the chunk-partial path;
   // the others a kernel without it (same arithmetic, leaner code)
   if (parts > 1)
     hipLaunchKernelGGL(attn_bf16_kernel<true>, grid, dim3(64), 0, s, static_cast<const uint16_t*>(q), q_stride,
                        static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache), block_table, ctx,
                        q_off, static_cast<uint16_t*>(out), q_len, Hq, Hkv, max_blocks, num_blocks, scale * kLog2e,
-                       seg_tokens, nseg_max, ws, items, blk_pos, n_rb, parts, 0);
+                       seg_tokens, nseg_max, ws, items, blk_pos, n_rb, parts, head_fastest ? 1 : 0);
   else
     hipLaunchKernelGGL(attn_bf16_kernel<false>, grid, dim3(64), 0, s, static_cast<const uint16_t*>(q), q_stride,
                        static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache), block_table, ctx,
