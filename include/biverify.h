@@ -161,7 +161,8 @@ biv_status gemm_bi(const void* A, const void* B, void* C, int64_t M, int64_t N, 
  * ctx [R] int32: verified context length L_r >= 0 of each request.
  * out [rows, Hq, D]                                dt, device
  *
- * Keys are cut into 256-token chunks aligned at absolute position 0.  Each
+ * Keys are cut into chunks of BIV_ATTN_CHUNK_TOKENS (512) tokens, aligned at
+ * absolute position 0 (256 tokens on the fp32 path).  Each
  * chunk gives a partial (max, sum, weighted values) for each row; partials
  * are left-folded in ascending chunk order within fixed segments of
  * BIV_ATTN_SEG_TOKENS tokens, and the segment results are left-folded in
@@ -173,7 +174,7 @@ biv_status gemm_bi(const void* A, const void* B, void* C, int64_t M, int64_t N, 
  * large grids add a one-workgroup launch before them that orders the
  * segments.  Where the grid of segments would hold fewer than 1024 waves
  * (decided by R, Hkv and max_blocks alone), each segment is taken by
- * several waves over consecutive 256-token chunks: the first folds its
+ * several waves over consecutive chunks: the first folds its
  * chunks, the later ones store their chunk partials, and a launch between
  * the two folds those on in the same ascending order, every segment of a
  * request at once -- the same fold, so the same bits.  The fp32 path folds all chunk partials of a row in one ascending
@@ -198,7 +199,7 @@ biv_status gemm_bi(const void* A, const void* B, void* C, int64_t M, int64_t N, 
  * results); it needs no initialisation.
  * Calls that share a workspace must be ordered (same stream).
  * ------------------------------------------------------------------------ */
-#define BIV_ATTN_CHUNK_TOKENS 256
+#define BIV_ATTN_CHUNK_TOKENS 512
 #define BIV_ATTN_SEG_TOKENS 4096
 
 size_t biv_attn_workspace_bytes(int R, int Hkv, int max_blocks, int seg_tokens);
@@ -223,9 +224,9 @@ biv_status attn_decode_bi(const void* q, int64_t q_stride, const void* k_cache, 
  * BIV_ATTN_SEG_TOKENS) <= BIV_ATTN_STATIC_SCRATCH_BYTES (32 MiB) and returns
  * BIV_EINVAL, launching nothing, when it needs more.  That covers, e.g., the
  * verify step of 64 requests x 8 KV heads at contexts up to 12288 (26 MB) or
- * one request up to 32768 (18 MB); batches small enough for their segments to be
- * split over several waves reserve room for every 256-token chunk's partial
- * (16 per segment) and reach the limit sooner.  Every call
+ * one request up to 32768 (10 MB); batches small enough for their segments to be
+ * split over several waves reserve room for every chunk's partial
+ * (8 per segment) and reach the limit sooner.  Every call
  * on a GPU shares that GPU's array (it keeps the last call's contents; the
  * kernels need no initialisation), so calls that overlap on one GPU -- on two
  * streams, or from two threads -- race: order them on one stream.  The

@@ -8,7 +8,7 @@
 // 0 .. ctx[r] + j.
 //
 // bf16 path.  The keys of a request are cut at fixed absolute positions:
-//   sub-tile = 32 keys (one MFMA block), chunk = 256 keys (the KV split),
+//   sub-tile = 32 keys (one MFMA block), chunk = 512 keys (the KV split),
 //   segment  = seg_tokens keys (4096 for the invariant kernel), taken by one
 //              wave, or split over several at small batch (see the kernel).
 // One 64-lane wave per (segment, KV head, row block) -- or per part of a
@@ -46,7 +46,12 @@ namespace biv {
 constexpr int kHD = 128;                 // head dim of the MFMA path
 constexpr int kSub = 32;                 // keys per sub-tile
 constexpr int kChunk = BIV_ATTN_CHUNK_TOKENS;
-constexpr int kSubsPerChunk = kChunk / kSub;
+// The non-invariant comparison path keeps 256-key chunks, so that it can cut
+// its segments at any multiple of 256 keys (its fold tree may vary with the
+// split; that is what it is for).
+constexpr int kAdaptiveChunk = 256;
+static_assert(kChunk % kSub == 0 && kAdaptiveChunk % kSub == 0 && kChunk % kAdaptiveChunk == 0, "chunk sizes");
+constexpr int kF32Chunk = 256;  // the fp32 path's chunk: four keys per lane
 constexpr int kSlot = kSub * kHD * 2;    // 8 KiB: K or V of one sub-tile
 constexpr int kRing = 5;                 // LDS slots per wave (40 KiB: four waves fill a CU's 160 KiB)
 static_assert(kRing == 5, "wait_ring: a full ring leaves four loads (32 copies) in flight");
@@ -225,7 +230,7 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
     const int32_t* __restrict__ q_off, uint16_t* __restrict__ out, int q_len, int Hq, int Hkv, int max_blocks,
     int num_blocks, float scale_log2,
     int seg_tokens, int nseg_max, AttnWs ws, const int32_t* __restrict__ items, int blk_pos, int n_rb, int parts,
-    int head_fastest) {
+    int head_fastest, int subs_per_chunk) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kRing * kSlot];
   // grid: (segment part, KV head, row block); (KV head, segment part, row
   // block) when head_fastest (no work list); or with a work list (parts
@@ -512,7 +517,7 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
     sv = sv + 2 >= kRing ? sv + 2 - kRing : sv + 2;
     // ---- end of a chunk: fold its partial into the segment result
     // (ascending), or, in a later part of a split segment, write it out
-    if ((s + 1) % kSubsPerChunk == 0 || s + 1 == nsub) {
+    if ((s + 1) % subs_per_chunk == 0 || s + 1 == nsub) {
       float o[64];
 #pragma unroll
       for (int d = 0; d < 4; ++d)
@@ -623,7 +628,7 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(const int32_t* __restri
 // Parts per segment: halve the parts' length while the grid of segments
 // holds fewer than kSplitBelow potential waves (one round of resident waves
 // on a 256-CU device: a CU streams fastest with all four of its wave slots
-// busy), down to one 256-token chunk per part.  From the call's shape alone.
+// busy), down to one chunk per part.  From the call's shape alone.
 constexpr int64_t kSplitBelow = 1024;
 static int attn_parts(int64_t Rv, int Hkv, int64_t nseg_max, int seg_tokens) {
   const int cps = seg_tokens / kChunk;
@@ -841,7 +846,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
                                                       int q_len, int Hq, int Hkv, int D, int max_blocks,
                                                       int num_blocks, float scale) {
   __shared__ float qs[128];
-  __shared__ float ps[kChunk];
+  __shared__ float ps[kF32Chunk];
   const int j = blockIdx.x, h = blockIdx.y, r = blockIdx.z;
   const int lane = threadIdx.x;
   const ReqRows rr = req_rows(q_off, r, q_len);
@@ -855,8 +860,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
   for (int d = lane; d < D; d += 64) qs[d] = q[qtok * q_stride + (int64_t)h * D + d];
   __syncthreads();
   float M = -INFINITY, Ls = 0.0f, O0 = 0.0f, O1 = 0.0f;
-  for (int cb = 0; cb < n_keys; cb += kChunk) {
-    const int ce = min(cb + kChunk, n_keys);
+  for (int cb = 0; cb < n_keys; cb += kF32Chunk) {
+    const int ce = min(cb + kF32Chunk, n_keys);
     float sv[4];
     float mx = -INFINITY;
 #pragma unroll
@@ -929,11 +934,14 @@ static biv_status check_attn(const char* who, const void* q, int64_t q_stride, c
 static inline int attn_blk_pos(int Hq, int Hkv) { return 32 / (Hq / Hkv); }
 static inline int attn_row_blocks(int q_len, int Hq, int Hkv) { return (int)cdiv(q_len, attn_blk_pos(Hq, Hkv)); }
 
+// invariant: the batch-invariant call (kChunk-key chunks; small batches'
+// segments split over waves, same bits); otherwise the comparison path
+// (kAdaptiveChunk-key chunks, one wave per segment).
 static biv_status launch_attn_bf16(const char* who, const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
                                    const int32_t* block_table, const int32_t* ctx, const int32_t* q_off, void* out,
                                    int R, int q_len,
                                    int Hq, int Hkv, int max_blocks, int num_blocks, float scale, int seg_tokens,
-                                   bool allow_split, void* workspace, size_t workspace_bytes, hipStream_t s) {
+                                   bool invariant, void* workspace, size_t workspace_bytes, hipStream_t s) {
   const int G = Hq / Hkv;
   BIV_REQUIRE(G >= 1 && 32 % G == 0, "%s: bf16 path needs Hq/Hkv dividing 32 (got %d)", who, G);
   const int blk_pos = attn_blk_pos(Hq, Hkv), n_rb = attn_row_blocks(q_len, Hq, Hkv);
@@ -941,14 +949,16 @@ static biv_status launch_attn_bf16(const char* who, const void* q, int64_t q_str
   const int Rv = R * n_rb;  // row blocks
   BIV_REQUIRE(aligned16(q) && aligned16(k_cache) && aligned16(v_cache) && q_stride % 8 == 0,
               "%s: q (and its row stride) and the caches must be 16-byte aligned", who);
-  BIV_REQUIRE(seg_tokens > 0 && seg_tokens % kChunk == 0, "%s: segment size %d is not a multiple of %d", who,
-              seg_tokens, kChunk);
+  // the invariant call's chunks, or the comparison path's
+  const int chunk = invariant ? kChunk : kAdaptiveChunk;
+  BIV_REQUIRE(seg_tokens > 0 && seg_tokens % chunk == 0, "%s: segment size %d is not a multiple of %d", who,
+              seg_tokens, chunk);
   const int64_t nseg_max64 = cdiv((int64_t)max_blocks * 16, seg_tokens);
   BIV_REQUIRE(nseg_max64 <= 0x7fffffff, "%s: too many segments", who);
   const int nseg_max = (int)nseg_max64;
   // Segments split over several waves where the grid would otherwise hold
   // few waves (decided by the call's shape alone; no bits change).
-  const int parts = allow_split ? attn_parts(Rv, Hkv, nseg_max, seg_tokens) : 1;
+  const int parts = invariant ? attn_parts(Rv, Hkv, nseg_max, seg_tokens) : 1;
   // the layout this launch uses (biv_attn_workspace_bytes, which allows for
   // splits, is never smaller)
   const size_t need = attn_ws_floats(Rv, Hkv, nseg_max, seg_tokens, parts) * sizeof(float);
@@ -983,12 +993,12 @@ static biv_status launch_attn_bf16(const char* who, const void* q, int64_t q_str
     hipLaunchKernelGGL(attn_bf16_kernel<true>, grid, dim3(64), 0, s, static_cast<const uint16_t*>(q), q_stride,
                        static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache), block_table, ctx,
                        q_off, static_cast<uint16_t*>(out), q_len, Hq, Hkv, max_blocks, num_blocks, scale * kLog2e,
-                       seg_tokens, nseg_max, ws, items, blk_pos, n_rb, parts, head_fastest ? 1 : 0);
+                       seg_tokens, nseg_max, ws, items, blk_pos, n_rb, parts, head_fastest ? 1 : 0, chunk / kSub);
   else
     hipLaunchKernelGGL(attn_bf16_kernel<false>, grid, dim3(64), 0, s, static_cast<const uint16_t*>(q), q_stride,
                        static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache), block_table, ctx,
                        q_off, static_cast<uint16_t*>(out), q_len, Hq, Hkv, max_blocks, num_blocks, scale * kLog2e,
-                       seg_tokens, nseg_max, ws, items, blk_pos, n_rb, 1, head_fastest ? 1 : 0);
+                       seg_tokens, nseg_max, ws, items, blk_pos, n_rb, 1, head_fastest ? 1 : 0, chunk / kSub);
   biv_status st = launched(who);
   if (st != BIV_OK || (nseg_max <= 1 && parts == 1)) return st;
   if (parts > 1) {  // complete the split segments, every segment of a request at once
@@ -1007,9 +1017,12 @@ static biv_status launch_attn_bf16(const char* who, const void* q, int64_t q_str
 
 extern "C" size_t biv_attn_workspace_bytes(int R, int Hkv, int max_blocks, int seg_tokens) {
   using namespace biv;
-  if (R <= 0 || Hkv <= 0 || max_blocks <= 0 || seg_tokens <= 0 || seg_tokens % kChunk != 0) return 0;
+  if (R <= 0 || Hkv <= 0 || max_blocks <= 0 || seg_tokens <= 0 || seg_tokens % kAdaptiveChunk != 0) return 0;
   const int64_t nseg = cdiv((int64_t)max_blocks * 16, seg_tokens);
-  return attn_ws_floats(R, Hkv, nseg, seg_tokens, attn_parts(R, Hkv, nseg, seg_tokens)) * sizeof(float);
+  // room for the split layout wherever the invariant call could split (its
+  // segments are whole chunks); the comparison path never splits
+  const int parts = seg_tokens % kChunk == 0 ? attn_parts(R, Hkv, nseg, seg_tokens) : 1;
+  return attn_ws_floats(R, Hkv, nseg, seg_tokens, parts) * sizeof(float);
 }
 
 extern "C" size_t biv_attn_workspace_bytes_q(int R, int q_len, int Hq, int Hkv, int max_blocks, int seg_tokens) {
@@ -1048,11 +1061,11 @@ extern "C" biv_status attn_decode_bi(const void* q, int64_t q_stride, const void
 
 extern "C" int biv_attn_adaptive_split(int R, int Hkv, int max_blocks) {
   using namespace biv;
-  if (R <= 0 || Hkv <= 0 || max_blocks <= 0) return kChunk;
+  if (R <= 0 || Hkv <= 0 || max_blocks <= 0) return kAdaptiveChunk;
   const int64_t cap = (int64_t)max_blocks * 16;
   const int64_t want = cdiv(1024, (int64_t)R * Hkv);  // segments per (request, head): one wave per SIMD
-  int64_t split = cdiv(cdiv(cap, want), kChunk) * kChunk;
-  return (int)std::max<int64_t>(kChunk, split);
+  int64_t split = cdiv(cdiv(cap, want), kAdaptiveChunk) * kAdaptiveChunk;
+  return (int)std::max<int64_t>(kAdaptiveChunk, split);
 }
 
 extern "C" biv_status attn_decode_adaptive(const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
@@ -1067,7 +1080,8 @@ extern "C" biv_status attn_decode_adaptive(const void* q, int64_t q_stride, cons
   if (R == 0) return BIV_OK;
   if (D != kHD) return fail(BIV_EUNSUPPORTED, "attn_decode_adaptive: supports D == 128 only (D=%d)", D);
   if (32 % (Hq / Hkv) != 0) return fail(BIV_EUNSUPPORTED, "attn_decode_adaptive: needs Hq/Hkv dividing 32");
-  BIV_REQUIRE(split_tokens >= 0 && split_tokens % kChunk == 0, "attn_decode_adaptive: split_tokens must be a multiple of %d", kChunk);
+  BIV_REQUIRE(split_tokens >= 0 && split_tokens % kAdaptiveChunk == 0,
+              "attn_decode_adaptive: split_tokens must be a multiple of %d", kAdaptiveChunk);
   const int split = split_tokens == 0 ? biv_attn_adaptive_split(R, Hkv, max_blocks) : split_tokens;
   return launch_attn_bf16("attn_decode_adaptive", q, q_stride, k_cache, v_cache, block_table, ctx, nullptr, out, R, q_len, Hq, Hkv,
                           max_blocks, num_blocks, scale, split, false, workspace, workspace_bytes,
