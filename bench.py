@@ -745,7 +745,7 @@ def micro_attention(torch, biv, iters):
             wsb = torch.empty(biv.attn_workspace_bytes(B, Hkv, lay.max_blocks), dtype=torch.uint8, device="cuda")
             run_bi = lambda i: biv.attn_decode_bi(q, kc, vc, bt, cx, ob, q_len, scale, wsb)
             t_bi, p90 = _event_times(torch, run_bi, iters, pre=flush.zero_)
-            # the comparison: the load-adaptive split, half of it and twice it (multiples of 256 tokens, its chunk,
+            # the comparison: the load-adaptive split, half of it and twice it (multiples of 256 tokens
             # within the block table's capacity), each timed, the fastest kept
             auto = biv.attn_adaptive_split(B, Hkv, lay.max_blocks)
             cap = -(-lay.max_blocks * 16 // 256) * 256

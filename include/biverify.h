@@ -161,8 +161,8 @@ biv_status gemm_bi(const void* A, const void* B, void* C, int64_t M, int64_t N, 
  * ctx [R] int32: verified context length L_r >= 0 of each request.
  * out [rows, Hq, D]                                dt, device
  *
- * Keys are cut into chunks of BIV_ATTN_CHUNK_TOKENS (512) tokens, aligned at
- * absolute position 0 (256 tokens on the fp32 path).  Each
+ * Keys are cut into chunks of BIV_ATTN_CHUNK_TOKENS (256) tokens, aligned at
+ * absolute position 0.  Each
  * chunk gives a partial (max, sum, weighted values) for each row; partials
  * are left-folded in ascending chunk order within fixed segments of
  * BIV_ATTN_SEG_TOKENS tokens, and the segment results are left-folded in
@@ -199,7 +199,7 @@ biv_status gemm_bi(const void* A, const void* B, void* C, int64_t M, int64_t N, 
  * results); it needs no initialisation.
  * Calls that share a workspace must be ordered (same stream).
  * ------------------------------------------------------------------------ */
-#define BIV_ATTN_CHUNK_TOKENS 512
+#define BIV_ATTN_CHUNK_TOKENS 256
 #define BIV_ATTN_SEG_TOKENS 4096
 
 size_t biv_attn_workspace_bytes(int R, int Hkv, int max_blocks, int seg_tokens);
@@ -224,9 +224,9 @@ biv_status attn_decode_bi(const void* q, int64_t q_stride, const void* k_cache, 
  * BIV_ATTN_SEG_TOKENS) <= BIV_ATTN_STATIC_SCRATCH_BYTES (32 MiB) and returns
  * BIV_EINVAL, launching nothing, when it needs more.  That covers, e.g., the
  * verify step of 64 requests x 8 KV heads at contexts up to 12288 (26 MB) or
- * one request up to 32768 (10 MB); batches small enough for their segments to be
+ * one request up to 32768 (18 MB); batches small enough for their segments to be
  * split over several waves reserve room for every chunk's partial
- * (8 per segment) and reach the limit sooner.  Every call
+ * (16 per segment) and reach the limit sooner.  Every call
  * on a GPU shares that GPU's array (it keeps the last call's contents; the
  * kernels need no initialisation), so calls that overlap on one GPU -- on two
  * streams, or from two threads -- race: order them on one stream.  The

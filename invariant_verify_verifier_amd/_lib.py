@@ -26,7 +26,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 BIV_OK, BIV_EINVAL, BIV_EUNSUPPORTED, BIV_EHIP = 0, 1, 2, 3
 BIV_F32, BIV_BF16 = 0, 1
 BIV_EPI_STORE, BIV_EPI_ACCUM, BIV_EPI_SWIGLU = 0, 1, 2
-ATTN_CHUNK_TOKENS = 512
+ATTN_CHUNK_TOKENS = 256
 ATTN_SEG_TOKENS = 4096
 
 _vp, _i32, _i64, _f32, _f64, _sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,

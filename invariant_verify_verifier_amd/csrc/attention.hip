@@ -8,7 +8,7 @@
 // 0 .. ctx[r] + j.
 //
 // bf16 path.  The keys of a request are cut at fixed absolute positions:
-//   sub-tile = 32 keys (one MFMA block), chunk = 512 keys (the KV split),
+//   sub-tile = 32 keys (one MFMA block), chunk = 256 keys (the KV split),
 //   segment  = seg_tokens keys (4096 for the invariant kernel), taken by one
 //              wave, or split over several at small batch (see the kernel).
 // One 64-lane wave per (segment, KV head, row block) -- or per part of a
@@ -46,12 +46,13 @@ namespace biv {
 constexpr int kHD = 128;                 // head dim of the MFMA path
 constexpr int kSub = 32;                 // keys per sub-tile
 constexpr int kChunk = BIV_ATTN_CHUNK_TOKENS;
-// The non-invariant comparison path keeps 256-key chunks, so that it can cut
-// its segments at any multiple of 256 keys (its fold tree may vary with the
-// split; that is what it is for).
+// The non-invariant comparison path's chunk: it cuts its segments at any
+// multiple of it (its fold tree may vary with the split; that is what it is
+// for).
 constexpr int kAdaptiveChunk = 256;
 static_assert(kChunk % kSub == 0 && kAdaptiveChunk % kSub == 0 && kChunk % kAdaptiveChunk == 0, "chunk sizes");
 constexpr int kF32Chunk = 256;  // the fp32 path's chunk: four keys per lane
+static_assert(kF32Chunk == kChunk, "both paths cut the keys at the same chunk boundaries");
 constexpr int kSlot = kSub * kHD * 2;    // 8 KiB: K or V of one sub-tile
 constexpr int kRing = 5;                 // LDS slots per wave (40 KiB: four waves fill a CU's 160 KiB)
 static_assert(kRing == 5, "wait_ring: a full ring leaves four loads (32 copies) in flight");

@@ -130,10 +130,10 @@ def test_workspace_sizes(lib):
     n = lib.biv_attn_workspace_bytes(64, 8, 513, 1024)
     nseg = -(-513 * 16 // 1024)
     assert n == 64 * 8 * nseg * (4096 + 128) * 4 + 64 * nseg * 4  # segment results + work list
-    # one request, contexts up to 32768: its 8 x 8 segment waves are split 8
-    # ways (one 512-token chunk each), with room for every chunk's partial
+    # one request, contexts up to 32768: its 8 x 8 segment waves are split 16
+    # ways (one 256-token chunk each), with room for every chunk's partial
     n1 = lib.biv_attn_workspace_bytes(1, 8, 2048, 4096)
-    assert n1 == (8 * 8 + 8 * 8 * 8) * (4096 + 128) * 4 + 8 * 4
+    assert n1 == (8 * 8 + 8 * 8 * 16) * (4096 + 128) * 4 + 8 * 4
     # the comparison path's splits are multiples of 256 tokens
     assert lib.biv_attn_workspace_bytes(1, 8, 2048, 256) == 8 * 128 * (4096 + 128) * 4 + 128 * 4
     assert lib.biv_attn_workspace_bytes(1, 8, 2048, 200) == 0

@@ -745,7 +745,7 @@ def _attn_ref(lay, kc, vc, q, q_len, dtype="bf16"):
 @pytest.mark.parametrize("q_len", [1, 8])
 def test_attention_bf16_parity(biv, q_len):
     """32 q heads / 8 KV heads x 128, paged KV (16-token pages, permuted),
-    contexts spanning several 512-token chunks and 4096-token segments plus
+    contexts spanning several 256-token chunks and 4096-token segments plus
     ragged tails and exact boundaries (sub-tile, chunk and segment ends; 15
     requests: segments split over several waves)."""
     ctx = [0, 255 - q_len + 1, 256, 512 - q_len, 513 - q_len, 1023, 1024, 1025, 2048 - q_len, 2049 - q_len, 2500,
@@ -797,7 +797,7 @@ def test_attention_bf16_batch_invariance(biv):
 @pytest.mark.parametrize("q_len", [1, 8])
 def test_attention_split_segments_equal_unsplit(biv, q_len):
     """A request alone is few segment waves, so each segment is split over
-    8 waves (later parts store per-chunk partials, completed by the chunk
+    16 waves (later parts store per-chunk partials, completed by the chunk
     fold before the segment fold); beside 63 other requests the grid holds
     at least 1024 waves and nothing is split.  Its rows are the same bits
     either way, across a split single segment, a part left without keys, a
@@ -935,7 +935,7 @@ def test_attention_adaptive_matches_oracle(biv):
 
 def test_attention_adaptive_any_split_fits_smallest_split_workspace(biv):
     """The load-adaptive call never splits a segment over waves, so a
-    workspace sized for its smallest segment (256 tokens, its chunk: the most segment
+    workspace sized for its smallest segment (256 tokens: the most segment
     partials) serves every larger one -- what a comparison pass that times
     several splits with one workspace relies on; each split still matches
     the oracle."""

@@ -51,7 +51,7 @@ def test_static_scratch_attention_equals_workspace_call(biv):
     ctx = list(wl.rng(200).integers(500, 8000, size=64))
     ref, got = _case(biv, ctx, 8, seed=201)
     assert np.array_equal(got, ref)
-    # second, smaller call (one request, one row: its segments split over 8
+    # second, smaller call (one request, one row: its segments split over 16
     # waves, chunk partials in the scratch) over what the first left there
     ref, got = _case(biv, [9000], 1, seed=210)
     assert np.array_equal(got, ref)
