@@ -825,6 +825,37 @@ def test_attention_split_segments_equal_unsplit(biv, q_len):
         out2 = bits(_run_attn(biv, lay2, kc2, vc2, q2, q_len))
         assert np.array_equal(out2[slot * q_len:(slot + 1) * q_len], alone), (q_len, L)
 
+@pytest.mark.parametrize("q_len", [1, 8])
+def test_attention_rows_equal_across_split_counts(biv, q_len):
+    """The same request in batches of 1, 8, 16, 32 and 64 over one block
+    table (three 4096-token segments per request at most) is taken by 16, 8,
+    4, 2 and 1 waves per segment: parts of one 256-token chunk, of several
+    chunks, and no split.  Its rows are the same bits in every batch."""
+    Hq, Hkv, D, R = 32, 8, 128, 64
+    ctx = [9000] + list(wl.rng(310).integers(50, 3000, size=R - 1))
+    lay, kc, vc, q = _attn_inputs(R, q_len, Hq, Hkv, D, ctx, seed=311)
+    nseg_max = -(-lay.max_blocks * 16 // biv.ATTN_SEG_TOKENS)
+    assert nseg_max == 3
+    kcd, vcd, qd = dev_bf16(kc), dev_bf16(vc), dev_bf16(q)
+    bt_all, cx_all = dev_i32(lay.block_table), dev_i32(lay.ctx)
+    rows = {}
+    for B in (1, 8, 16, 32, 64):
+        potential, parts = B * Hkv * nseg_max, 1
+        while 16 % (2 * parts) == 0 and potential * parts < 1024:
+            parts *= 2
+        announce("attention split counts", q_len, B, parts)
+        out = torch.full((B * q_len, Hq, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+        ws = torch.zeros(biv.attn_workspace_bytes(B, Hkv, lay.max_blocks, q_len=q_len, Hq=Hq), dtype=torch.uint8,
+                         device=DEV)
+        biv.attn_decode_bi(qd[:B * q_len], kcd, vcd, bt_all[:B].contiguous(), cx_all[:B].contiguous(), out, q_len,
+                           1.0 / math.sqrt(D), ws)
+        sync()
+        rows[parts] = bits(out)[:q_len].copy()
+    assert sorted(rows) == [1, 2, 4, 8, 16]
+    for parts, r in rows.items():
+        assert np.array_equal(r, rows[1]), (q_len, parts)
+
+
 def test_attention_bf16_verify_rows_equal_single_decodes(biv):
     """Row j of a K=8 verify block equals, bit for bit, the same query decoded
     alone (K=1) at context L+j: extra masked keys and chunks fold as no-ops."""
