@@ -677,23 +677,22 @@ static int resident_attn_waves() {
 }
 
 // Second pass for requests with more than one segment or a split segment:
-// per segment, in ascending order, its partial from the first pass and --
-// for a split segment -- the partials of its later chunks, folded on in
-// ascending order (completing the segment's left fold over its chunks);
-// then the segment results left-folded in ascending order from the first
-// one (the fold above, element by element), and the output written.  Four
+// per segment, in ascending order, its result -- from the first pass, or,
+// for a split segment, as attn_chunk_fold_kernel completed it (the first
+// part's fold with the later chunks folded on in ascending order) -- and
+// the segment results left-folded in ascending order from the first one
+// (the fold above, element by element), and the output written.  Four
 // workgroups of 256 threads per (KV head, row block) (measured: 1-7% faster
 // than one of 1024, same bits); thread t of workgroup z takes lane t % 64 of
 // the first pass and its values 4q .. 4q+3, q = 4z + t / 64 (dims
 // 32(q/4) + 8(q%4) + 4g .. +3 of row (t%64) % 32).  Up to kCombBatch segment
-// partials, and kChunkBatch chunk partials, are loaded at once.
+// partials are loaded at once.
 //
-// When segments were split, attn_chunk_fold_kernel completes every split
-// segment first, all segments of a request in parallel (the chain of folds
-// is what bounds this pass at small batch), and the second pass then folds
-// segments only (chunks_folded).  The folds and their order are the same.
+// Split segments are completed before this pass, all segments of a request
+// in parallel (a chain of chunk folds inside this pass was what bounded it
+// at small batch).
 constexpr int kCombZ = 4;  // workgroups per (KV head, row block)
-constexpr int kCombThreads = 1024 / kCombZ, kCombBatch = 8, kChunkBatch = 4, kChunkFoldBatch = 8;
+constexpr int kCombThreads = 1024 / kCombZ, kCombBatch = 8, kChunkFoldBatch = 8;
 
 // A split segment's partial: the fold of its first part's chunks from the
 // first pass, then its later chunks folded on in ascending order; written to
@@ -758,7 +757,7 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(const int32_
                                                                     uint16_t* __restrict__ out, int q_len, int Hq,
                                                                     int Hkv, int max_blocks, int seg_tokens,
                                                                     int nseg_max, AttnWs ws, int blk_pos, int n_rb,
-                                                                    int parts, int chunks_folded) {
+                                                                    int parts) {
   const int kvh = blockIdx.x, v = blockIdx.y;  // v: row block, as in the first pass
   const int r = v / n_rb, j0 = (v - r * n_rb) * blk_pos;
   const int tid = threadIdx.x, q = blockIdx.z * (kCombThreads / 64) + (tid >> 6), lane = tid & 63, g = lane >> 5,
@@ -768,7 +767,7 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(const int32_
   if (jn <= 0) return;
   const int n_tok = min(ctx[r] + j0 + jn, max_blocks * 16);
   const int nseg = (n_tok + seg_tokens - 1) / seg_tokens;
-  const int part_tok = seg_tokens / parts, cps = seg_tokens / kChunk, cpp = part_tok / kChunk;
+  const int part_tok = seg_tokens / parts, cps = seg_tokens / kChunk;
   // keys of segment s; it was split when they exceed one part
   auto seg_keys = [&](int sg) { return min((sg + 1) * seg_tokens, n_tok) - sg * seg_tokens; };
   if ((nseg <= 1 && seg_keys(0) <= part_tok) || li >= nrows) return;  // written by the first pass
@@ -780,8 +779,8 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(const int32_
 #pragma unroll
     for (int b = 0; b < kCombBatch; ++b) {
       if (s0 + b < nseg) {
-        // a split segment completed by attn_chunk_fold_kernel sits in its first chunk slot
-        const bool done = chunks_folded && seg_keys(s0 + b) > part_tok;
+        // a split segment, completed by attn_chunk_fold_kernel, sits in its first chunk slot
+        const bool done = seg_keys(s0 + b) > part_tok;
         const int64_t sl = done ? (slot0 + s0 + b) * cps : slot0 + s0 + b;
         const float* po = done ? ws.chunk_o : ws.part_o;
         const float* pml = done ? ws.chunk_ml : ws.part_ml;
@@ -796,27 +795,6 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(const int32_
     for (int b = 0; b < kCombBatch; ++b) {
       const int sg = s0 + b;
       if (sg >= nseg) continue;
-      const int keys = seg_keys(sg);
-      if (!chunks_folded && keys > part_tok) {  // split: the segment's chunks after its first part, kChunkBatch at a time
-        const int nch = (keys + kChunk - 1) / kChunk;
-        for (int c0 = cpp; c0 < nch; c0 += kChunkBatch) {
-          float co[kChunkBatch][4], cm[kChunkBatch], cl[kChunkBatch];
-#pragma unroll
-          for (int e = 0; e < kChunkBatch; ++e) {
-            if (c0 + e < nch) {
-              const int64_t cs = slot0 * cps + (int64_t)sg * cps + c0 + e;
-              const f32x4 w = *(reinterpret_cast<const f32x4*>(ws.chunk_o + cs * 4096) + q * 64 + lane);
-#pragma unroll
-              for (int c = 0; c < 4; ++c) co[e][c] = w[c];
-              cm[e] = ws.chunk_ml[cs * 128 + lane * 2 + 0];
-              cl[e] = ws.chunk_ml[cs * 128 + lane * 2 + 1];
-            }
-          }
-#pragma unroll
-          for (int e = 0; e < kChunkBatch; ++e)
-            if (c0 + e < nch) fold_into<4>(m[b], l[b], o[b], cm[e], cl[e], co[e]);
-        }
-      }
       if (sg == 0) {
         M = m[b];
         Lt = l[b];
@@ -1010,7 +988,7 @@ static biv_status launch_attn_bf16(const char* who, const void* q, int64_t q_str
     if (st != BIV_OK) return st;
   }
   hipLaunchKernelGGL(attn_combine_kernel, dim3(Hkv, Rv, kCombZ), dim3(kCombThreads), 0, s, ctx, q_off, static_cast<uint16_t*>(out),
-                     q_len, Hq, Hkv, max_blocks, seg_tokens, nseg_max, ws, blk_pos, n_rb, parts, parts > 1 ? 1 : 0);
+                     q_len, Hq, Hkv, max_blocks, seg_tokens, nseg_max, ws, blk_pos, n_rb, parts);
   return launched(who);
 }
 
