@@ -870,6 +870,29 @@ def test_attention_bf16_verify_rows_equal_single_decodes(biv):
         assert np.array_equal(one[0], block[j]), f"row {j}"
 
 
+@pytest.mark.parametrize("G", [2, 8, 32])
+@pytest.mark.parametrize("q_len", [1, 8])
+def test_attention_bf16_gqa_ratios(biv, q_len, G):
+    """Other query-to-KV head ratios G (dividing 32): a 32-row block then holds
+    32/G positions of G heads (16, 4 or 1 positions), so a verify step of 8
+    positions takes 1, 2 or 8 row blocks.  Parity with the oracle on contexts
+    from empty to three segments, and each request alone (its segments split
+    over more waves) the same bits as in the batch."""
+    Hkv = 2
+    Hq = Hkv * G
+    ctx = [0, 300, 4097 - q_len, 9000]
+    lay, kc, vc, q = _attn_inputs(len(ctx), q_len, Hq, Hkv, 128, ctx, seed=400 + G + q_len)
+    announce("attention bf16 GQA ratio", G, q_len)
+    out = _run_attn(biv, lay, kc, vc, q, q_len)
+    check_bf16(f64(out), _attn_ref(lay, kc, vc, q, q_len), f"attention bf16 G={G} q_len={q_len}")
+    full = bits(out)
+    for r in (1, 3):
+        lay1 = wl.PagedLayout(ctx=lay.ctx[r:r + 1], q_len=q_len, block_table=lay.block_table[r:r + 1],
+                              num_blocks=lay.num_blocks, max_blocks=lay.max_blocks)
+        one = bits(_run_attn(biv, lay1, kc, vc, q[r * q_len:(r + 1) * q_len], q_len))
+        assert np.array_equal(one, full[r * q_len:(r + 1) * q_len]), f"G={G} q_len={q_len} request {r}"
+
+
 @pytest.mark.parametrize("q_len,G", [(33, 4), (200, 4), (70, 1)])
 def test_attention_bf16_row_blocks_prefill(biv, q_len, G):
     """q_len beyond one 32-row block (a prefill, or a long verify): the rows
