@@ -1038,7 +1038,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the verifier step shards by request with no inter-GPU traffic; see the design notes)",
+              "(the verifier step would shard by request, with no traffic between GPUs)",
               file=sys.stderr)
         sys.exit(2)
     import torch

@@ -15,7 +15,9 @@ Citations name the page and the paragraph a function follows:
 
 Where the pages are silent (RoPE convention, layer order, norm epsilon, what
 happens when all K candidates are accepted, ...) the plainest reading is
-taken; each such reading is listed in the design notes of the repository.
+taken, and the function or section that takes it says which (the RoPE
+section header, the decoder's pre-norm layer order, verify's rule for an
+all-accepted request).
 """
 from __future__ import annotations
 
