@@ -1037,7 +1037,7 @@ def main():
         tree_bench(args)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the verifier step would shard by request, with no traffic between GPUs)",
               file=sys.stderr)
         sys.exit(2)

@@ -28,8 +28,8 @@
  *   - All work is enqueued asynchronously on `stream` (a hipStream_t; NULL =
  *     the default stream).  Nothing synchronises.
  *   - Arguments are checked on the host before anything is launched; a bad
- *     argument returns BIV_EINVAL (or BIV_EUNSUPPORTED for a shape this build
- *     has no kernel for) and launches nothing.  biv_last_error() then holds
+ *     argument returns BIV_EINVAL (or BIV_EUNSUPPORTED for a shape the
+ *     library has no kernel for) and launches nothing.  biv_last_error() then holds
  *     a message (thread-local).  A failed launch returns BIV_EHIP.  Device
  *     faults surface at the caller's next synchronisation.
  *   - No C++ exception crosses this interface.
@@ -55,7 +55,7 @@ extern "C" {
 typedef enum {
   BIV_OK = 0,
   BIV_EINVAL = 1,       /* bad argument: null pointer, size, alignment, dtype */
-  BIV_EUNSUPPORTED = 2, /* valid request this build has no kernel for */
+  BIV_EUNSUPPORTED = 2, /* valid request the library has no kernel for */
   BIV_EHIP = 3          /* the HIP runtime reported an error */
 } biv_status;
 
