@@ -464,21 +464,21 @@ def test_gemm_bf16_exact_integer_operands(biv):
     assert np.array_equal(c.cpu().numpy().astype(np.float64), oracle.linear(a, b))
 
 
-def _cfg1_weight(N=14336, K=4096):
+def _microbench_weight(N=14336, K=4096):
     """The microbench weight is [4096, 14336] ~ N(0, 0.02); the GEMM takes it in
     linear-layer layout [N, K] (a one-time transpose, off the timed path)."""
     w = wl.normal_bf16(12, (K, N), std=0.02)
     return np.ascontiguousarray(w.T)
 
 
-def test_gemm_bf16_cfg1_parity_and_invariance(biv):
+def test_gemm_bf16_14336x4096_microbench_parity_and_invariance(biv):
     """[M, 4096] x [4096, 14336], bf16 in, fp32 accumulate; every row's bits
     identical for M = 1, 2, 4, ..., 512 and under a row shuffle."""
     K, N = 4096, 14336
     a_np = wl.normal_bf16(10, (512, K))
-    w_np = _cfg1_weight(N, K)
+    w_np = _microbench_weight(N, K)
     a, w = dev_bf16(a_np), dev_bf16(w_np)
-    announce("gemm bf16 cfg1 M=512")
+    announce("gemm bf16 14336x4096 M=512")
     c = torch.empty((512, N), dtype=torch.bfloat16, device=DEV)
     biv.gemm_bi(a, w, c)
     cf = torch.empty((512, N), dtype=torch.float32, device=DEV)
