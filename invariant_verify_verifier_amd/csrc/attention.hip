@@ -95,8 +95,8 @@ struct AttnWs {
 };
 
 // Partial (m, l, o[64]) of a lane -> slot `slot` of (po, pml): sixteen 1 KiB
-// stores of four values each (streaming stores for segment partials; chunk
-// partials, few and read back soon, go through the caches), then m and l.
+// stores of four values each, with the non-temporal hint when kStream, then
+// m and l.
 // Lanes of rows past the row block's last (live false) store nothing: the
 // combine never reads them, and at one query position per request only 4 of
 // the 32 rows are real.
@@ -561,9 +561,16 @@ __global__ __launch_bounds__(64, 1) void attn_bf16_kernel(
     return;
   }
   // the segment result (or, for a split segment, the fold of its first
-  // part's chunks) -> workspace; attn_combine_kernel folds on from there
-  store_partial<true>(ws.part_o, ws.part_ml, ((int64_t)v * Hkv + kvh) * nseg_max + seg, lane, row_ok, Ms, Ls,
-                      Os);
+  // part's chunks) -> workspace; attn_combine_kernel folds on from there.
+  // Grids of about one round of waves store it through the caches, where
+  // the fold that follows finds it (the 8B-shaped pass's attention 2.8%
+  // faster); grids long enough for a work list stream it past them (2.5%
+  // faster at 64 requests of U[512, 32768], whose partials are many).
+  const int64_t pslot = ((int64_t)v * Hkv + kvh) * nseg_max + seg;
+  if (items)
+    store_partial<true>(ws.part_o, ws.part_ml, pslot, lane, row_ok, Ms, Ls, Os);
+  else
+    store_partial<false>(ws.part_o, ws.part_ml, pslot, lane, row_ok, Ms, Ls, Os);
 }
 
 // Work list for large grids: every full segment first, then the partial last
